@@ -1,0 +1,43 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
+the pins catch each one.  The oracle source itself is never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "mla_oracle.c")
+
+# (name, text in the source, replacement)
+MUTANTS = [
+    ("matvec_transposed_operand", "acc += A[(size_t)i * n + j] * x[j];", "acc += A[(size_t)j * m + i % m] * x[j % m];"),
+    ("rope_term_dropped", "double rope = d_r > 0 ? mla_oracle_dot(d_r, q_r, KR + (size_t)t * d_r) : 0.0;",
+     "double rope = 0.0;"),
+    ("explicit_rope_key_dropped", "if (d_r > 0) memcpy(K + (size_t)t * dq + d_h, rope_row(P, b, t), sizeof(double) * d_r);",
+     "if (d_r > 0) memset(K + (size_t)t * dq + d_h, 0, sizeof(double) * d_r);"),
+    ("causal_offset_off_by_one", "const int vis = L - n_q + m + 1; /* tokens 0 .. L - n_q + m */",
+     "const int vis = L - n_q + m; /* tokens 0 .. L - n_q + m */"),
+    ("softmax_max_not_subtracted_wrong_sign", "p[t] = exp(s[t] - mx);", "p[t] = exp(mx - s[t]);"),
+    ("page_row_index", "(size_t)(t % P->page_size)) * P->d_c", "(size_t)(t / P->page_size)) * P->d_c"),
+    ("scale_ignored", "s[t] = scale * (content + rope);", "s[t] = (content + rope);"),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor missing: " + name
+    mutated = src.replace(old, new)
+    c_file = tmp_path / "mutant.c"
+    c_file.write_text(mutated)
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", "-o", str(so), str(c_file), "-lm"],
+                   check=True)
+    env = dict(os.environ, MLA_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pages.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_identities.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "planted mistake %s passed every pin:\n%s" % (name, r.stdout[-2000:])

@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of one absorbed-MLA decode step on one MI355X.
+
+A step is one call of the whole hot path (query absorption, split-context
+attention over the latent + RoPE cache, log-sum-exp combine, W_UV
+up-projection) on one batch of synthetic DeepSeek-V2-shaped inputs that are
+already resident in HBM.  To keep the 256 MB Infinity Cache from serving the
+cache and weights, steps rotate over enough distinct device copies
+("layers") of the cache and weights to exceed 1 GiB.
+
+Prints ONE JSON line on stdout (progress goes to stderr).  `value` is the
+algorithmic attention TFLOP/s of the whole step (FLOPs counted as 4 h d_c +
+2 h d_r + h per visible (query, cached token) pair plus 2 h d_h d_c per query
+row for each of the two projections, softmax excluded); `cache_gbps` is the
+latent + RoPE cache bytes per step over the step time.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode attention TFLOP/s + latent-cache GB/s (h=128,d_c=512) @ T=4K..128K"
+HBM_GBPS = 8000.0          # MI355X HBM3E peak
+MFMA_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+MFMA_F32_TFLOPS = 157.3
+MIN_ROTATION_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "q_absorb": "q_absorb.hip", "split_attn": "split_attn.hip", "combine": "combine.hip",
+    "up_project": "up_project.hip",
+}
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def counts(wl, splits):
+    """Algorithmic bytes and FLOPs of one step, per kernel."""
+    el = 2 if wl.dtype == "bf16" else 4
+    R = wl.rows
+    pairs = wl.visible_pairs()
+    per_pair = 4 * wl.h * wl.d_c + 2 * wl.h * wl.d_r + wl.h
+    proj_flops = 2 * R * wl.h * wl.d_h * wl.d_c
+    w_bytes = wl.h * wl.d_h * wl.d_c * el
+    cache_bytes = wl.cache_tokens() * (wl.d_c + wl.d_r) * el
+    part_bytes = R * splits * wl.h * (wl.d_c + 1) * 4
+    return {
+        "q_absorb": dict(bytes=w_bytes + R * wl.h * (wl.d_h * el + wl.d_c * 2), flops=proj_flops),
+        "split_attn": dict(bytes=cache_bytes, flops=pairs * per_pair, partial_bytes=part_bytes),
+        "combine": dict(bytes=part_bytes + R * wl.h * wl.d_c * 2, flops=0),
+        "up_project": dict(bytes=w_bytes + R * wl.h * (wl.d_c * 2 + wl.d_h * el), flops=proj_flops),
+        "step": dict(bytes=cache_bytes + 2 * w_bytes, flops=pairs * per_pair + 2 * proj_flops,
+                     cache_bytes=cache_bytes),
+    }
+
+
+def kernel_roofline(name, c, avg_s, dtype):
+    """Bound, achieved and peak for one kernel from its algorithmic counts."""
+    peak_flops = MFMA_BF16_TFLOPS if dtype == "bf16" else MFMA_F32_TFLOPS
+    ridge = peak_flops * 1e12 / (HBM_GBPS * 1e9)
+    ai = c["flops"] / c["bytes"] if c["bytes"] else float("inf")
+    if c["flops"] and ai > ridge:
+        achieved = c["flops"] / avg_s / 1e12
+        return dict(bound="mfma", achieved=achieved, peak=peak_flops, unit="TFLOP/s",
+                    frac=achieved / peak_flops)
+    achieved = c["bytes"] / avg_s / 1e9
+    return dict(bound="hbm", achieved=achieved, peak=HBM_GBPS, unit="GB/s", frac=achieved / HBM_GBPS)
+
+
+def source_digest(kernel):
+    csrc = os.path.join(ROOT, "mla_latent_cache_absorbed_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.h", "kernels.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        e = t[kernel][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("source_digest") != source_digest(kernel):
+        return None
+    return e.get("bytes_per_launch")
+
+
+class Layers:
+    """Distinct device copies of the cache, queries and weights of a workload."""
+
+    def __init__(self, dw, n):
+        import torch
+        keys = ("q", "q_r", "latent_pool", "rope_pool", "w_uk", "w_uv")
+        self.sets = [dict(dw.t)]
+        for _ in range(n - 1):
+            d = dict(dw.t)
+            for k in keys:
+                d[k] = dw.t[k].clone()
+            self.sets.append(d)
+        torch.cuda.synchronize()
+
+    def __len__(self):
+        return len(self.sets)
+
+
+def layer_bytes(wl):
+    el = 2 if wl.dtype == "bf16" else 4
+    return el * (wl.num_pages * wl.page_size * (wl.d_c + wl.d_r) + 2 * wl.h * wl.d_h * wl.d_c)
+
+
+def time_steps(dw, layers, steps, warmup, per_kernel):
+    """Average step time (s); with per_kernel, also per-kernel averages (s)."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding
+    n = len(layers)
+    for i in range(warmup):
+        dw.run(**layers.sets[i % n])
+    torch.cuda.synchronize()
+    if per_kernel:
+        binding.mla_decode_enable_timing(dw.dec.plan, steps)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        dw.run(**layers.sets[(warmup + i) % n])
+    end.record()
+    torch.cuda.synchronize()
+    step_s = start.elapsed_time(end) / 1e3 / steps
+    kernels = None
+    if per_kernel:
+        ms, runs = binding.mla_decode_read_timing(dw.dec.plan)
+        binding.mla_decode_enable_timing(dw.dec.plan, 0)
+        kernels = {k: v / 1e3 / runs for k, v in ms.items()}
+    return step_s, kernels
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """Time the fp64 oracle (explicit K/V form, as it stands) on a bounded
+    sample of the workload: whole decode of a subset of (sequence, head)
+    pairs, sized for about target_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    from mla_latent_cache_absorbed_amd import inputs
+    prob = oracle.Problem(**inputs.oracle_problem_kwargs(wl))
+    threads = oracle.num_threads()
+    all_pairs = [(b, i) for b in range(wl.batch) for i in range(wl.h)]
+
+    def run(n):
+        pairs = all_pairs[:n]
+        t = time.perf_counter()
+        oracle.decode_explicit(prob, pairs)
+        return time.perf_counter() - t, pairs
+
+    n = min(len(all_pairs), max(1, threads))
+    dt, pairs = run(n)
+    if dt < target_s / 3:
+        n = int(min(len(all_pairs), max(n, round(n * target_s / max(dt, 1e-3)))))
+        dt, pairs = run(n)
+    per_pair = 4 * wl.d_c + 2 * wl.d_r + 1
+    flops = 0
+    for b, _ in pairs:
+        L = int(wl.lens[b])
+        flops += sum(L - wl.n_q + m + 1 for m in range(wl.n_q)) * per_pair
+        flops += wl.n_q * 2 * 2 * wl.d_h * wl.d_c
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=min(threads, len(pairs)),
+                kind="oracle",
+                sample="explicit fp64 oracle (per-head K/V rebuilt, textbook softmax) on %d of "
+                       "%d (sequence, head) pairs of %s, %.1f s wall" % (len(pairs), len(all_pairs),
+                                                                        wl.name, dt),
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ds2_t4k")
+    ap.add_argument("--extra", default="ds2_t32k",
+                    help="second workload whose split kernel is also measured ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="0 = enough for 1 GiB")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_latent_cache_absorbed_amd import inputs
+    from mla_latent_cache_absorbed_amd.runner import DeviceWorkload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    def measure(name, steps, warmup):
+        wl = inputs.make(name)
+        dw = DeviceWorkload(wl)
+        n_layers = args.layers or max(2, min(60, math.ceil(MIN_ROTATION_BYTES / layer_bytes(wl))))
+        layers = Layers(dw, n_layers)
+        splits, chunk = dw.split_plan()
+        log("%s: %d layers rotated (%.0f MB each), %d chunks of %d tokens" %
+            (name, n_layers, layer_bytes(wl) / 1e6, splits, chunk))
+        step_s, _ = time_steps(dw, layers, steps, warmup, per_kernel=False)
+        _, kern = time_steps(dw, layers, steps, 2, per_kernel=True)
+        c = counts(wl, splits)
+        del layers
+        return wl, dw, c, step_s, kern, splits, chunk, n_layers
+
+    wl, dw, c, step_s, kern, splits, chunk, n_layers = measure(args.workload, args.steps, args.warmup)
+    log("step %.2f us; kernels (us): %s" % (step_s * 1e6, {k: round(v * 1e6, 2) for k, v in kern.items()}))
+
+    rooflines = {k: kernel_roofline(k, c[k], kern[k], wl.dtype) for k in kern}
+    dominant = max(kern, key=lambda k: kern[k])
+    roof = dict(rooflines[dominant])
+    roof["kernel"] = dominant
+    roof["avg_us"] = kern[dominant] * 1e6
+    traffic = measured_traffic(dominant, wl.name)
+    roof["traffic"] = traffic
+    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel", "avg_us")}
+
+    out = {
+        "metric": METRIC,
+        "value": c["step"]["flops"] / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q,
+                   "context": int(wl.max_len), "h": wl.h, "d_c": wl.d_c, "d_r": wl.d_r,
+                   "d_h": wl.d_h, "page_size": wl.page_size, "splits": splits,
+                   "chunk_len": chunk, "layers_rotated": n_layers},
+        "cache_gbps": c["step"]["cache_bytes"] / step_s / 1e9,
+        "roofline": roof,
+        "kernels": {k: dict(avg_us=kern[k] * 1e6, **rooflines[k]) for k in kern},
+    }
+
+    if args.extra:
+        wl2, dw2, c2, step2, kern2, s2, ch2, nl2 = measure(args.extra, max(10, args.steps // 2), 5)
+        out["split_kernel_" + wl2.name] = dict(
+            avg_us=kern2["split_attn"] * 1e6, splits=s2, chunk_len=ch2,
+            cache_gbps=c2["split_attn"]["bytes"] / kern2["split_attn"] / 1e9,
+            tflops=c2["split_attn"]["flops"] / kern2["split_attn"] / 1e12,
+            step_us=step2 * 1e6, kernels_us={k: v * 1e6 for k, v in kern2.items()},
+            roofline=kernel_roofline("split_attn", c2["split_attn"], kern2["split_attn"], wl2.dtype))
+        del dw2
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

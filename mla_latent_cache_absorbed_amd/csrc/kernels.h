@@ -1,0 +1,58 @@
+// kernels.h -- internal launch interface between the host plan and the
+// gfx950 kernels.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Everything the four steps of one decode call need, already validated.
+struct DecodeArgs {
+  int batch, n_q, h, d_c, d_r, d_h;
+  int page_size, max_pages, num_pages, max_len;
+  int splits;      // chunks per sequence (S)
+  int chunk_len;   // tokens per chunk
+  int in_bf16;     // storage type of q, q_r, caches, weights
+  int out_bf16;    // storage type of o
+  float scale_log2;  // softmax scale * log2(e)
+
+  const void* q;
+  const void* q_r;
+  const void* latent_pool;
+  const void* rope_pool;
+  const int32_t* page_table;
+  const int32_t* context_lens;
+  const void* w_uk;
+  const void* w_uv;
+  void* out;
+
+  // workspace carve-up
+  void* q_abs;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
+  float* part_o;    // [R][S][h][d_c]   f32, chunk results already normalised
+  float* part_lse;  // [R][S][h]        f32, base-2 log-sum-exp of each chunk
+  void* c_bar;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
+};
+
+// Heads handled by one work-group of the fast split kernel.
+constexpr int kFastHeadsPerGroup = 64;
+// Tokens staged per LDS tile in the fast split kernel.
+constexpr int kFastTile = 32;
+
+// Fast path: bf16 storage, d_c = 512, d_r = 64, d_h = 128, h % 64 == 0,
+// page_size % 32 == 0.
+hipError_t launch_q_absorb_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_up_project_bf16(const DecodeArgs& a, hipStream_t s);
+
+// General path: any dims (d_c <= 1024), f32 or bf16 storage, f32 math.
+hipError_t launch_q_absorb_general(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_split_attn_general(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_up_project_general(const DecodeArgs& a, hipStream_t s);
+
+// Shared by both paths: log-sum-exp merge of the chunk results into c_bar
+// (bf16 when cbar_bf16, else f32).
+hipError_t launch_combine(const DecodeArgs& a, bool cbar_bf16, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle, on the
+same seeded inputs, for the five configurations and their edge cases.
+
+Tolerance (normwise, max |gpu - oracle| / max |oracle|): 1e-2 for bf16
+storage with fp32 accumulation, 1e-5 for the fp32 mode.  Full-size
+configurations are checked on sampled (sequence, head) pairs with the
+absorbed fp64 form (itself pinned equal to the explicit K/V form) plus a
+few pairs with the explicit form.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mla_latent_cache_absorbed_amd import inputs
+from tests._parity import check, gpu_rows, log, problem, sample_pairs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+def _run(wl, torch, **kw):
+    from mla_latent_cache_absorbed_amd.runner import DeviceWorkload
+    dw = DeviceWorkload(wl, **kw)
+    log("%s: splits/chunk = %s" % (wl.name, dw.split_plan()))
+    dw.run()
+    torch.cuda.synchronize()
+    return dw
+
+
+# --------------------------------------------------------------------------
+# configuration 1: tiny fp32 (general path), whole output, every split count
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("splits", [0, 1, 2, 4])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_tiny_fp32(torch, splits, out_dtype):
+    wl = inputs.make("tiny_fp32")
+    dw = _run(wl, torch, num_splits=splits, out_dtype=out_dtype)
+    ref = oracle.decode_explicit(problem(wl))
+    got = dw.result_f64()
+    assert got.shape == ref.shape == (1, 1, 4, 16)
+    check(got, ref, "f32" if out_dtype == "f32" else "bf16", "tiny_fp32 S=%d out=%s" % (splits, out_dtype))
+
+
+# --------------------------------------------------------------------------
+# configuration 2: T = 4096, all heads (absorbed oracle) + explicit sample
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("splits", [0, 1, 16])
+def test_ds2_t4k(torch, splits):
+    wl = inputs.make("ds2_t4k")
+    dw = _run(wl, torch, num_splits=splits)
+    got = dw.result_f64()
+    prob = problem(wl)
+    ref = oracle.decode_absorbed(prob)
+    check(got, ref, "bf16", "ds2_t4k S=%d all heads" % splits)
+    if splits == 0:
+        pairs = sample_pairs(wl, 4)
+        check(gpu_rows(got, pairs), oracle.decode_explicit(prob, pairs), "bf16",
+              "ds2_t4k explicit sample")
+
+
+def test_ds2_t4k_fp32_output_matches_bf16_output(torch):
+    wl = inputs.make("ds2_t4k")
+    a = _run(wl, torch, out_dtype="f32").result_f64()
+    b = _run(wl, torch, out_dtype="bf16").result_f64()
+    ref = oracle.decode_absorbed(problem(wl))
+    check(a, ref, "bf16", "ds2_t4k fp32 output")
+    # the bf16 output is the fp32 one rounded to nearest
+    assert np.max(np.abs(a - b)) <= np.max(np.abs(a)) * 2.0 ** -8
+
+
+# --------------------------------------------------------------------------
+# configuration 3: batched, paged, shuffled, variable lengths
+# --------------------------------------------------------------------------
+def test_ds2_paged_b32(torch):
+    wl = inputs.make("ds2_paged_b32")
+    log("lengths %s" % wl.lens.tolist())
+    dw = _run(wl, torch)
+    got = dw.result_f64()
+    prob = problem(wl)
+    pairs = sample_pairs(wl, 4)
+    check(gpu_rows(got, pairs), oracle.decode_absorbed(prob, pairs), "bf16",
+          "ds2_paged_b32 absorbed, 4 heads x 32 sequences")
+    few = pairs[::32][:4]
+    check(gpu_rows(got, few), oracle.decode_explicit(prob, few), "bf16",
+          "ds2_paged_b32 explicit sample")
+
+
+def test_paging_permutation_is_bitwise_invisible(torch):
+    """The same logical cache under another page permutation gives the same bits."""
+    wl = inputs.make("ds2_paged_b32")
+    dw = _run(wl, torch)
+    first = dw.out.clone()
+    rng = np.random.default_rng(77)
+    perm = rng.permutation(wl.num_pages)  # new pool position of each old page
+    inv = np.argsort(perm)
+    lat = dw.t["latent_pool"][torch.from_numpy(inv).cuda()].contiguous()
+    rope = dw.t["rope_pool"][torch.from_numpy(inv).cuda()].contiguous()
+    table = torch.from_numpy(perm[wl.page_table].astype(np.int32)).cuda()
+    dw.run(latent_pool=lat, rope_pool=rope, page_table=table)
+    torch.cuda.synchronize()
+    assert torch.equal(first, dw.out)
+
+
+# --------------------------------------------------------------------------
+# configuration 4: T = 131072, forced chunk counts 64 / 128 / 256
+# --------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def t128k_ref():
+    wl = inputs.make("ds2_t128k")
+    prob = problem(wl)
+    pairs = sample_pairs(wl, 8)
+    return wl, pairs, oracle.decode_absorbed(prob, pairs), prob
+
+
+@pytest.mark.parametrize("splits", [64, 128, 256])
+def test_ds2_t128k(torch, t128k_ref, splits):
+    wl, pairs, ref, prob = t128k_ref
+    dw = _run(wl, torch, num_splits=splits)
+    assert dw.split_plan() == (splits, 131072 // splits)
+    got = dw.result_f64()
+    check(gpu_rows(got, pairs), ref, "bf16", "ds2_t128k S=%d, 8 heads" % splits)
+    if splits == 128:
+        one = pairs[:1]
+        check(gpu_rows(got, one), oracle.decode_explicit(prob, one), "bf16",
+              "ds2_t128k explicit, 1 head")
+
+
+# --------------------------------------------------------------------------
+# configuration 5: 4 causal query tokens per sequence
+# --------------------------------------------------------------------------
+def test_ds2_mtp_b16(torch):
+    wl = inputs.make("ds2_mtp_b16")
+    dw = _run(wl, torch)
+    got = dw.result_f64()
+    prob = problem(wl)
+    pairs = sample_pairs(wl, 2)
+    check(gpu_rows(got, pairs), oracle.decode_absorbed(prob, pairs), "bf16",
+          "ds2_mtp_b16 absorbed, 2 heads x 16 sequences")
+    few = pairs[:2]
+    check(gpu_rows(got, few), oracle.decode_explicit(prob, few), "bf16",
+          "ds2_mtp_b16 explicit sample")
+    # the four rows differ (the causal mask is applied per query token)
+    assert np.max(np.abs(got[0, 0] - got[0, 3])) > 1e-3
+
+
+def test_ds2_t32k(torch):
+    wl = inputs.make("ds2_t32k")
+    dw = _run(wl, torch)
+    got = dw.result_f64()
+    pairs = sample_pairs(wl, 16)
+    check(gpu_rows(got, pairs), oracle.decode_absorbed(problem(wl), pairs), "bf16",
+          "ds2_t32k absorbed, 16 heads")
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_ragged_lengths_and_tails(torch, splits):
+    """Lengths that end inside a tile and inside a page, down to one token."""
+    wl = inputs.make("ds2_t4k", batch=6, lens=("list", [1, 31, 33, 97, 300, 2049]),
+                     shuffled=True, seed=201)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16",
+          "ragged lengths S=%d" % splits)
+
+
+def test_single_token_context_returns_projected_latent(torch):
+    wl = inputs.make("ds2_t4k", lens=("fixed", 1), seed=202)
+    dw = _run(wl, torch, out_dtype="f32")
+    ref = oracle.decode_explicit(problem(wl))
+    check(dw.result_f64(), ref, "bf16", "one cached token")
+
+
+@pytest.mark.parametrize("L", [4, 5, 37, 64])
+def test_multi_token_short_contexts(torch, L):
+    """n_q = 4 with contexts so short that the causal diagonal spans tiles."""
+    wl = inputs.make("ds2_mtp_b16", batch=2, lens=("list", [L, L + 29]), seed=203 + L)
+    dw = _run(wl, torch, num_splits=0)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "n_q=4 L=%d" % L)
+
+
+def test_full_table_capacity(torch):
+    """max_context_len equal to the page-table capacity."""
+    wl = inputs.make("ds2_t4k", batch=2, lens=("list", [640, 640]), shuffled=True, seed=204)
+    assert wl.max_pages * wl.page_size == 640
+    dw = _run(wl, torch)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "full table capacity")
+
+
+def test_repeat_runs_are_bitwise_identical(torch):
+    wl = inputs.make("ds2_paged_b32")
+    dw = _run(wl, torch)
+    first = dw.out.clone()
+    for _ in range(3):
+        dw.run()
+    torch.cuda.synchronize()
+    assert torch.equal(first, dw.out)
+
+
+def test_general_path_bf16_odd_shapes(torch):
+    """bf16 storage with shapes outside the MFMA kernels (general path)."""
+    wl = inputs.make("tiny_fp32", dtype="bf16", h=6, d_c=40, d_r=6, d_h=12, page_size=8,
+                     batch=3, n_q=2, lens=("list", [2, 19, 50]), shuffled=True, seed=205)
+    dw = _run(wl, torch, num_splits=0)
+    check(dw.result_f64(), oracle.decode_explicit(problem(wl)), "bf16", "general bf16")
+
+
+def test_general_path_fp32_without_rope(torch):
+    wl = inputs.make("tiny_fp32", d_r=0, batch=2, lens=("list", [64, 7]), seed=206)
+    dw = _run(wl, torch, num_splits=3)
+    check(dw.result_f64(), oracle.decode_explicit(problem(wl)), "f32", "general fp32 d_r=0")
+
+
+def test_empty_batch_is_a_no_op(torch):
+    from mla_latent_cache_absorbed_amd import binding
+    wl = inputs.make("ds2_t4k", lens=("fixed", 64), seed=207)
+    dw = _run(wl, torch)
+    before = dw.out.clone()
+    t = dw.t
+    binding.mla_decode_run(dw.dec.plan, 0, 1, 64, wl.num_pages, t["q"], t["q_r"],
+                           t["latent_pool"], t["rope_pool"], t["page_table"],
+                           t["context_lens"], t["w_uk"], t["w_uv"], dw.out, dw.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(before, dw.out)
+
+
+def test_runs_on_a_side_stream(torch):
+    wl = inputs.make("ds2_t4k", lens=("fixed", 512), seed=208)
+    dw = _run(wl, torch)
+    ref = dw.out.clone()
+    dw.out.zero_()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dw.run()
+    s.synchronize()
+    assert torch.equal(ref, dw.out)

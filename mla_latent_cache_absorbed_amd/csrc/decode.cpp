@@ -94,6 +94,8 @@ Split plan_splits(const mla_decode_plan& p, int batch, int n_q, int max_len) {
     s = std::min(std::max(want, 1), cap);
   }
   s = std::min(std::max(s, 1), std::max(1, ceil_div(max_len, gran)));
+  if (p.fast)  // the fast split kernel keeps at most kMaxFastChunkTiles tiles per chunk
+    s = std::max(s, ceil_div(max_len, (long long)mla::kMaxFastChunkTiles * mla::kFastTile));
   Split r;
   r.chunk_len = ceil_div(ceil_div(max_len, s), gran) * gran;
   r.splits = std::max(1, ceil_div(max_len, r.chunk_len));
@@ -108,11 +110,11 @@ struct Layout {
 
 Layout layout_for(const mla_decode_plan& p, int batch, int n_q, int splits) {
   const size_t R = (size_t)batch * n_q, h = p.cfg.h, d_c = p.cfg.d_c;
-  const size_t inter = p.fast ? 2 : 4;  // bytes per q_abs / c_bar element
+  const size_t inter = p.fast ? 2 : 4;  // bytes per q_abs / partial / c_bar element
   Layout l;
   l.q_abs = 0;
   l.part_o = l.q_abs + align256(R * h * d_c * inter);
-  l.part_lse = l.part_o + align256(R * splits * h * d_c * 4);
+  l.part_lse = l.part_o + align256(R * splits * h * d_c * inter);
   l.c_bar = l.part_lse + align256(R * splits * h * 4);
   l.total = l.c_bar + align256(R * h * d_c * inter);
   return l;
@@ -260,7 +262,7 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
   a.out = out;
   char* ws = static_cast<char*>(workspace);
   a.q_abs = ws + l.q_abs;
-  a.part_o = reinterpret_cast<float*>(ws + l.part_o);
+  a.part_o = ws + l.part_o;
   a.part_lse = reinterpret_cast<float*>(ws + l.part_lse);
   a.c_bar = ws + l.c_bar;
 

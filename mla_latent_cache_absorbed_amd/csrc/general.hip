@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64) void split_general_kernel(DecodeArgs a) {
   }
 
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  float* po = a.part_o + (((size_t)r * a.splits + split) * a.h + head) * a.d_c;
+  float* po = static_cast<float*>(a.part_o) + (((size_t)r * a.splits + split) * a.h + head) * a.d_c;
 #pragma unroll
   for (int j = 0; j < kMaxPerLane; ++j) {
     const int f = lane + 64 * j;

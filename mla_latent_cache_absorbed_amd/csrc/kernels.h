@@ -30,7 +30,8 @@ struct DecodeArgs {
 
   // workspace carve-up
   void* q_abs;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
-  float* part_o;    // [R][S][h][d_c]   f32, chunk results already normalised
+  void* part_o;     // [R][S][h][d_c]   chunk results already normalised: bf16
+                    //                  (fast path) or f32 (general path)
   float* part_lse;  // [R][S][h]        f32, base-2 log-sum-exp of each chunk
   void* c_bar;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
 };
@@ -39,6 +40,9 @@ struct DecodeArgs {
 constexpr int kFastHeadsPerGroup = 64;
 // Tokens staged per LDS tile in the fast split kernel.
 constexpr int kFastTile = 32;
+// Largest chunk (in tiles) the fast split kernel accepts: it keeps the pool
+// row of every tile of its chunk in LDS.
+constexpr int kMaxFastChunkTiles = 1024;
 
 // Fast path: bf16 storage, d_c = 512, d_r = 64, d_h = 128, h % 64 == 0,
 // page_size % 32 == 0.
@@ -51,8 +55,8 @@ hipError_t launch_q_absorb_general(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_split_attn_general(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_up_project_general(const DecodeArgs& a, hipStream_t s);
 
-// Shared by both paths: log-sum-exp merge of the chunk results into c_bar
-// (bf16 when cbar_bf16, else f32).
-hipError_t launch_combine(const DecodeArgs& a, bool cbar_bf16, hipStream_t s);
+// Log-sum-exp merge of the chunk results into c_bar: bf16 partials and
+// c_bar on the fast path, f32 on the general path.
+hipError_t launch_combine(const DecodeArgs& a, bool fast, hipStream_t s);
 
 }  // namespace mla

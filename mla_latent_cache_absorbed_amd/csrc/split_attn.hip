@@ -5,8 +5,8 @@
 //   s_t   = scale * (q_abs . C[t] + q_R . K_R[t])        (score)
 //   p_t   = exp(s_t - m) with the running max m           (online softmax)
 //   acc   = sum_t p_t C[t],  l = sum_t p_t                (latent accumulation)
-// and writes the chunk's normalised latent acc / l and its base-2
-// log-sum-exp.  The cache is contracted last for the scores and first for
+// and writes the chunk's normalised latent acc / l (bf16) and its base-2
+// log-sum-exp (fp32).  The cache is contracted last for the scores and first for
 // the values, which is the cheapest association for a single query ("MLA,
 // dim by dim" section 4.2 and the cached-decode chains of section 5.2; the
 // concatenated content + RoPE dot product of "Mathematical Prerequisites for
@@ -16,27 +16,32 @@
 // values ("MLA, dim by dim", FLOPs table of section 5.2).
 //
 // gfx950 design
-// - 256 threads = 4 wave64s; each wave owns 16 heads.  Every 32-token tile
-//   of latent + RoPE rows is read from HBM once per work-group with 16-byte
-//   loads (8 lanes per 128-byte line) and staged in LDS, where all 64 heads
-//   reuse it.
+// - 256 threads = 4 wave64s, 16 heads per wave, one work-group per CU (the
+//   fp32 accumulator and the bf16 query need most of the 512-entry register
+//   file of one wave per SIMD).
+// - The chunk is streamed in 32-token tiles through a ring of four LDS
+//   stages filled by direct global->LDS DMA (global_load_lds_dwordx4): no
+//   registers are spent on staging and three tiles are in flight while a
+//   fourth is consumed.  A tile never straddles a cache page (pages are multiples of
+//   32 tokens), so each tile is one contiguous run of 32 latent rows and 32
+//   RoPE rows in the pool; the pool row of every tile is looked up once at
+//   the start.  Every latent row is read from HBM once per work-group with
+//   1 KB per instruction, and all 64 heads of the group reuse it from LDS.
+// - The tile stays token-major in LDS with its 16-byte chunks XOR-swizzled
+//   per row, so that both read patterns below are free of bank conflicts.
 // - Scores: S^T[token][head] = KV[token][:] . Q[head][:] on 16x16x32 bf16
 //   MFMA, tokens as M, heads as N, K over the 576 latent + RoPE features.
 //   The absorbed query (bf16) stays in registers for the whole chunk.
-// - With heads as N, each lane holds one head's scores for 8 tokens, so the
+// - With heads as N each lane holds one head's scores for 8 tokens, so the
 //   running max and the rescale of the accumulator are per-lane values; the
 //   tile maximum needs two cross-lane steps.
 // - Latent accumulation: O^T[feature][head] += C^T[feature][token] .
 //   P^T[token][head], features as M (32 blocks of 16), heads as N, tokens as
-//   K.  The probabilities come straight out of the score accumulators in the
-//   B-operand layout (the k order is permuted identically on both sides), so
-//   no shuffle is needed.  The A operand needs the tile feature-major; it is
-//   written to LDS a second time, transposed, with a 4-token XOR swizzle so
-//   that both the transposing writes and the 8-byte MFMA reads spread over
-//   the LDS banks.
-// - The accumulator (64 heads x 512 features, fp32) lives in registers: 128
-//   per lane; with the query operands that needs one wave per SIMD (one
-//   work-group per CU), so the 512-entry register file is available.
+//   K.  The feature-major A operand comes straight from the token-major tile
+//   through the transposing LDS read ds_read_b64_tr_b16 (within 16 lanes,
+//   lane i receives element i & 3 of the 8-byte chunk addressed by lane
+//   4e + (i >> 2), for e = 0..3).  The probabilities come out of the score
+//   accumulators already in the matching B-operand order.
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.
@@ -53,15 +58,71 @@ constexpr int kDkv = kDc + kDr;
 constexpr int kTile = kFastTile;          // 32 tokens
 constexpr int kWaves = kFastHeadsPerGroup / 16;
 constexpr int kThreads = 64 * kWaves;     // 256
-constexpr int kKvStride = kDkv + 8;       // token-major row, elements (1168 B)
-constexpr int kCtStride = kTile + 8;      // feature-major row, elements (80 B)
-constexpr int kLdsKv = kTile * kKvStride;
-constexpr int kLdsCt = kDc * kCtStride;
-constexpr int kLdsBytes = (kLdsKv + kLdsCt) * 2;
-constexpr int kLatChunks = kTile * kDc / 8 / kThreads;  // 16-byte chunks per thread (8)
+constexpr int kStages = 4;                // LDS ring depth (three tiles in flight)
+constexpr int kLatBytes = kTile * kDc * 2;    // 32 KB: 32 rows of 1 KB
+constexpr int kRopeBytes = kTile * kDr * 2;   // 4 KB: 32 rows of 128 B
+constexpr int kStageBytes = kLatBytes + kRopeBytes;
 
-static_assert(kThreads == 256, "load mapping assumes 256 threads");
-static_assert(kTile * kDr / 8 == kThreads, "one RoPE chunk per thread");
+static_assert(kThreads == 256 && kTile == 32, "load mapping assumes 4 waves and 32-token tiles");
+// Largest factor (as a power of two) by which a weight may exceed 1 before
+// the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
+constexpr float kRescaleSlack = 8.0f;
+
+#define AS3 __attribute__((address_space(3)))
+typedef short tr_vec __attribute__((vector_size(8)));  // operand type of the transposing read
+
+// Swizzle of the 16-byte chunk index within latent row r of a tile (only
+// r mod 16 matters).  Chosen so that the score operand reads (16 rows, one
+// chunk) and the transposing reads (8 rows, two chunks) both hit distinct
+// banks with 32 or with 64 LDS banks.
+__device__ __forceinline__ int lat_swz(int r) {
+  const int k = (r >> 2) & 1;
+  return (k ^ ((r >> 3) & 1)) | ((r & 3) << 1) | (k << 3);
+}
+// Same for the 8 chunks of a 128-byte RoPE row.
+__device__ __forceinline__ int rope_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+
+// One wave-wide DMA of 64 x 16 bytes from global memory into LDS: lane l
+// reads sbase + voff[l] (a uniform 64-bit base in SGPRs plus a per-lane
+// 32-bit offset) and writes lds_base + 16 l.  Issued by hand so that the
+// compiler does not serialise the ring with conservative waits; completion
+// is tracked with explicit vmcnt waits below.  No output registers are
+// involved; M0 (the LDS base of the DMA) is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// The four lanes l, l^16, l^32, l^48 hold the same head (different tokens):
+// reduce across them with the gfx950 cross-row swaps instead of LDS
+// permutes.  permlane16_swap(x, x) leaves {x[l], x[l^16]} in the two
+// results (in some order) and permlane32_swap(x, x) {x[l], x[l^32]}.
+__device__ __forceinline__ float max_over_token_lanes(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_token_lanes(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 struct SplitArgs {
   const uint16_t* q_abs;        // [R][h][512]
@@ -70,23 +131,17 @@ struct SplitArgs {
   const uint16_t* rope_pool;    // [P][page][64]
   const int32_t* page_table;    // [B][max_pages]
   const int32_t* context_lens;  // [B]
-  float* part_o;                // [R][S][h][512]
+  uint16_t* part_o;             // [R][S][h][512] bf16
   float* part_lse;              // [R][S][h]
   int batch, n_q, h, head_groups, splits, chunk_len;
   int page_size, max_pages, num_pages, max_len;
   float scale_log2;
 };
 
-__device__ __forceinline__ int page_of(const SplitArgs& p, int b, int t) {
-  int pg = p.page_table[(size_t)b * p.max_pages + t / p.page_size];
-  pg = pg < 0 ? 0 : pg;
-  return pg >= p.num_pages ? p.num_pages - 1 : pg;
-}
 
 __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* kv = lds;           // [32][kKvStride]   token-major latent | rope
-  uint16_t* ct = lds + kLdsKv;  // [512][kCtStride]  feature-major latent, swizzled
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
+  __shared__ int tile_row[kMaxFastChunkTiles];
 
   // ---- which (sequence, chunk, query token, head group) this group owns ----
   const int sharers = p.n_q * p.head_groups;
@@ -111,18 +166,72 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   const int g = lane >> 4, l16 = lane & 15;
   const int head = hgi * kFastHeadsPerGroup + 16 * wave + l16;
 
-  float* po = p.part_o + (((size_t)r * p.splits + split) * p.h + head) * kDc;
+  uint16_t* po = p.part_o + (((size_t)r * p.splits + split) * p.h + head) * kDc;
   float* pl = p.part_lse + ((size_t)r * p.splits + split) * p.h + head;
 
   if (t0 >= t1) {  // nothing visible in this chunk for this query row
 #pragma unroll 4
-    for (int fb = 0; fb < kDc / 16; ++fb)
-      *reinterpret_cast<float4*>(po + fb * 16 + 4 * g) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int fb = 0; fb < kDc / 16; ++fb) *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) = make_uint2(0, 0);
     if (g == 0) *pl = -INFINITY;
     return;
   }
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;  // <= kMaxFastChunkTiles (host-checked)
 
-  // ---- absorbed query and RoPE query: MFMA B operands, kept in registers ----
+  f32x4 acc[kDc / 16];
+#pragma unroll
+  for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)ring);
+  static_assert(kStages * kStageBytes + kMaxFastChunkTiles * 4 <= 160 * 1024, "LDS budget");
+
+  // Tile i -> stage i % kStages: wave w copies latent rows 8w..8w+7 (one
+  // 1 KB row per DMA) and RoPE rows 8w..8w+7 (one DMA); row0 is the pool row
+  // of the tile's first token.  Rows past the end of the chunk repeat the
+  // tile's first row, so the LDS never holds non-finite garbage; their
+  // probabilities are exactly 0.  Exactly 9 DMAs per wave per tile; all
+  // address arithmetic is scalar except the per-lane offsets fixed here.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t lat_voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(8 * wave_u + j));
+  const int rope_row = 8 * wave_u + (lane >> 3);
+  const uint32_t rope_chunk = 16u * (uint32_t)((lane & 7) ^ rope_swz(rope_row));
+  const uint32_t rope_voff = (uint32_t)rope_row * (kDr * 2) + rope_chunk;
+  auto issue = [&](int i, int row0) {
+    const int ts = t0 + i * kTile;
+    const int nvalid = min(kTile, t1 - ts);
+    const uint32_t sb = ring_base + (uint32_t)((i % kStages) * kStageBytes);
+    const uint8_t* lat_tile = reinterpret_cast<const uint8_t*>(p.latent_pool) + (size_t)row0 * (kDc * 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int rr = 8 * wave_u + j;
+      lds_dma16(lat_tile + (rr < nvalid ? rr : 0) * (kDc * 2), lat_voff[j], sb + rr * (kDc * 2));
+    }
+    const uint8_t* rope_tile = reinterpret_cast<const uint8_t*>(p.rope_pool) + (size_t)row0 * (kDr * 2);
+    const uint32_t voff = nvalid == kTile ? rope_voff : (rope_row < nvalid ? rope_voff : rope_chunk);
+    lds_dma16(rope_tile, voff, sb + kLatBytes + 8 * wave_u * (kDr * 2));
+  };
+  auto tile_pool_row = [&](int i) {
+    const int ts = t0 + i * kTile;
+    int pg = p.page_table[(size_t)b * p.max_pages + ts / p.page_size];
+    pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+    return pg * p.page_size + ts % p.page_size;
+  };
+
+  // ---- prologue, ordered to shorten the chain of HBM latencies: the first
+  //      tiles' page lookups and DMAs go out first, then the query loads,
+  //      then the page lookups of the remaining tiles ----
+  {
+    // all lookups first (one wait), then the DMAs
+    int row[kStages - 1];
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i) row[i] = i < ntiles ? tile_pool_row(i) : 0;
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (i < ntiles) issue(i, row[i]);
+  }
+
   bf16x8 qa[kDc / 32], qr[kDr / 32];
   {
     const uint16_t* qa_row = p.q_abs + ((size_t)r * p.h + head) * kDc;
@@ -134,143 +243,172 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     for (int s = 0; s < kDr / 32; ++s)
       qr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr_row + 32 * s + 8 * g));
   }
+  for (int i = kStages - 1 + tid; i < ntiles; i += kThreads) tile_row[i] = tile_pool_row(i);
+  // Consume the query registers here: waiting for them also drains the
+  // prologue DMAs (older in the same counter), after which the ring's vmcnt
+  // bookkeeping owns the counter.
+#pragma unroll
+  for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
+#pragma unroll
+  for (int s = 0; s < kDr / 32; ++s) asm volatile("" :: "v"(qr[s]));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // tile_row is visible, the first tiles are in LDS
 
-  f32x4 acc[kDc / 16];
+  // Per-lane LDS byte offsets of the two read patterns within a stage; the
+  // remaining parts of every address are compile-time immediates.
+  //  score reads: row l16 (+16 tb), chunk 4s + g -> (4s) ^ c1_x with
+  //               c1_x = g ^ lat_swz(l16) < 16, i.e. base[s & 3] + 256 (s >> 2)
+  //  transposing reads: row 4g + e (+16 tb), chunk 2 fb + (q >> 1), half q & 1
+  //               -> base[fb & 7] + 256 (fb >> 3)
+  const int c1_x = g ^ lat_swz(l16);
+  const int rope_x = g ^ rope_swz(l16);
+  const int tr_row = 4 * g + (l16 >> 2);
+  const int tr_x = ((l16 & 3) >> 1) ^ lat_swz(tr_row);
+  uint32_t c1_base[4], rope_base[2], tr_base[8];
 #pragma unroll
-  for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int k2 = 0; k2 < 4; ++k2) c1_base[k2] = l16 * (kDc * 2) + 16 * ((4 * k2) ^ c1_x);
+#pragma unroll
+  for (int k2 = 0; k2 < 2; ++k2) rope_base[k2] = kLatBytes + l16 * (kDr * 2) + 16 * ((4 * k2) ^ rope_x);
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2)
+    tr_base[k2] = tr_row * (kDc * 2) + 16 * ((2 * k2) ^ tr_x) + 8 * (l16 & 1);
 
-  // ---- load mapping: latent chunk j of this thread = token lt, features
-  //      8 (lpc + 8 j) .. +7; RoPE chunk = token rt, features 8 rc .. +7 ----
-  const int lt = (lane >> 3) + 8 * wave;
-  const int lpc = lane & 7;
-  const int rt = tid >> 3, rc = tid & 7;
-
-  // Global -> LDS staging of one tile, in two halves so that at most five
-  // 16-byte loads per thread are in flight (the accumulator and the query
-  // already hold most of the register file).  The other work-group on the
-  // CU computes while this one waits on HBM.
-  auto load_stage = [&](int ts) {
-    const int gt = ts + lt;
-    const bool lat_ok = gt < t1;
-    const uint16_t* src = p.latent_pool;
-    if (lat_ok) {
-      const int pg = page_of(p, b, gt);
-      src += ((size_t)pg * p.page_size + gt % p.page_size) * kDc + 8 * lpc;
-    }
-    const int gr = ts + rt;
-    uint4 rope = make_uint4(0, 0, 0, 0);
-    if (gr < t1) {
-      const int pg = page_of(p, b, gr);
-      rope = *reinterpret_cast<const uint4*>(p.rope_pool + ((size_t)pg * p.page_size + gr % p.page_size) * kDr + 8 * rc);
-    }
-    // element (feature f, token t) of the transposed copy sits at
-    // ct[f][t ^ 4 sigma(f)], sigma(f) = (f >> 3) & 7 = lpc for this thread
-    const int tcol = lt ^ (4 * lpc);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint4 lat[kLatChunks / 2];
-#pragma unroll
-      for (int j = 0; j < kLatChunks / 2; ++j)
-        lat[j] = lat_ok ? *reinterpret_cast<const uint4*>(src + 64 * (j + half * kLatChunks / 2))
-                        : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < kLatChunks / 2; ++j) {
-        const int pc = lpc + 8 * (j + half * kLatChunks / 2);
-        *reinterpret_cast<uint4*>(&kv[lt * kKvStride + 8 * pc]) = lat[j];
-        const uint32_t w4[4] = {lat[j].x, lat[j].y, lat[j].z, lat[j].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          ct[(8 * pc + e) * kCtStride + tcol] = static_cast<uint16_t>(w4[e >> 1] >> (16 * (e & 1)));
+  // The rescale of the accumulator (rare: the reference maximum only moves
+  // when a score exceeds it by more than kRescaleSlack) lives outside the
+  // inner tile loop, which breaks out to it and then resumes at the same
+  // tile, recomputing its scores.  Keeping every VALU use of the
+  // accumulator out of the hot loop lets it stay in the MFMA registers.
+  int it = 0;
+  bool arrived = false;  // tile `it` already waited for and its successor issued
+  float tmax = -INFINITY;
+  while (it < ntiles) {
+    for (; it < ntiles; ++it) {
+      const int ts = t0 + it * kTile;
+      if (!arrived) {
+        // Tile `it` has landed once only the DMAs of the tiles after it (9
+        // per tile per wave, at most kStages - 2 tiles) are pending.
+        static_assert(kStages == 4, "the waits below count DMAs for a four-stage ring");
+        const int ahead = ntiles - 1 - it;
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        block_barrier();  // every wave's part of tile `it` is in LDS, tile it-1 is consumed
+        if (it + kStages - 1 < ntiles) issue(it + kStages - 1, tile_row[it + kStages - 1]);
       }
-    }
-    *reinterpret_cast<uint4*>(&kv[rt * kKvStride + kDc + 8 * rc]) = rope;
-  };
+      arrived = false;
 
-  const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-  for (int it = 0; it < ntiles; ++it) {
-    const int ts = t0 + it * kTile;
-    __syncthreads();  // every wave is done with the previous tile
-    load_stage(ts);
-    __syncthreads();
+      const AS3 uint8_t* stage = (const AS3 uint8_t*)ring + (it % kStages) * kStageBytes;
 
-    // ---- scores: S^T[tb*16 + 4g + j][head] ----
+    // ---- scores: S^T[tb*16 + 4g + j][head]; operands prefetched one step ahead ----
+    auto score_operand = [&](int s, int tb) -> bf16x8 {
+      const AS3 uint8_t* src = s < kDc / 32
+          ? stage + c1_base[s & 3] + 256 * (s >> 2) + tb * 16 * (kDc * 2)
+          : stage + rope_base[s - kDc / 32] + tb * 16 * (kDr * 2);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(src));
+    };
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      bf16x8 cur0 = score_operand(0, 0), cur1 = score_operand(0, 1);
 #pragma unroll
-    for (int s = 0; s < kDkv / 32; ++s) {
-      const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(&kv[(tb * 16 + l16) * kKvStride + 32 * s + 8 * g]));
-        sacc[tb] = mfma16x16x32(av, bq, sacc[tb]);
+      for (int s = 0; s < kDkv / 32; ++s) {
+        bf16x8 nxt0 = cur0, nxt1 = cur1;
+        if (s + 1 < kDkv / 32) {
+          nxt0 = score_operand(s + 1, 0);
+          nxt1 = score_operand(s + 1, 1);
+        }
+        const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
+        sacc[0] = mfma16x16x32(cur0, bq, sacc[0]);
+        sacc[1] = mfma16x16x32(cur1, bq, sacc[1]);
+        cur0 = nxt0;
+        cur1 = nxt1;
       }
-      // keep only a few operand loads in flight (register budget)
-      if ((s & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- online softmax (base 2), per lane = per head ----
-    float sv[8];
-    float tmax = -INFINITY;
+    // m_run is a reference maximum, not necessarily the exact running max;
+    // the final division by l_run makes the result independent of it.
+    // Scores stay unscaled until the exponent (scale > 0, so maxima commute).
+    if (ts + kTile > t1) {  // the chunk's last tile: tokens past t1 weigh 0
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (ts + tb * 16 + 4 * g + j >= t1) sacc[tb][j] = -INFINITY;
+    }
+    tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                 fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    tmax = max_over_token_lanes(tmax) * p.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
+      arrived = true;
+      break;  // rescale outside the hot loop, then redo this tile
+    }
+    f32x8 pf;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = ts + tb * 16 + 4 * g + j;
-        const float v = t < t1 ? sacc[tb][j] * p.scale_log2 : -INFINITY;
-        sv[tb * 4 + j] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = xor_max(tmax, 16);
-    tmax = xor_max(tmax, 32);
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    uint32_t pk[4];
-    float psum = 0.f;
+      for (int j = 0; j < 4; ++j)
+        pf[tb * 4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][j], p.scale_log2, -m_run));
+    const bf16x8 pb = __builtin_convertvector(pf, bf16x8);  // round to nearest even
+    {
+      // sum of the weights the MFMA sees (bf16), two per dot2
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint16_t b0 = f32_to_bf16(exp2f(sv[e] - m_use));
-      const uint16_t b1 = f32_to_bf16(exp2f(sv[e + 1] - m_use));
-      psum += bf16_to_f32(b0) + bf16_to_f32(b1);  // normalise by the weights the MFMA sees
-      pk[e >> 1] = static_cast<uint32_t>(b0) | (static_cast<uint32_t>(b1) << 16);
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 two = {pb[e], pb[e + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(two, one, psum, false);
+      }
+      l_run += psum;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const bf16x8 pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
     // ---- latent accumulation: O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
+    auto latent_operand = [&](int fb) -> bf16x8 {
+      const AS3 uint8_t* a0 = stage + tr_base[fb & 7] + 256 * (fb >> 3);
+      const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)a0));
+      const u16x4 hi = __builtin_bit_cast(
+          u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)(a0 + 16 * (kDc * 2))));
+      const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return as_bf16x8(v);
+    };
+    {
+      bf16x8 cur = latent_operand(0);
 #pragma unroll
-    for (int fb = 0; fb < kDc / 16; ++fb) {
-      const int f = fb * 16 + l16;
-      const int sig = (f >> 3) & 7;
-      const uint16_t* row = &ct[f * kCtStride];
-      const uint2 lo = *reinterpret_cast<const uint2*>(row + 4 * (g ^ sig));
-      const uint2 hi = *reinterpret_cast<const uint2*>(row + 4 * ((4 + g) ^ sig));
-      acc[fb] *= alpha;
-      acc[fb] = mfma16x16x32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pb, acc[fb]);
-      if ((fb & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int fb = 0; fb < kDc / 16; ++fb) {
+        bf16x8 nxt = cur;
+        if (fb + 1 < kDc / 16) nxt = latent_operand(fb + 1);
+        acc[fb] = mfma16x16x32(cur, pb, acc[fb]);
+        cur = nxt;
+      }
     }
+    }
+    if (it >= ntiles) break;
+    // ---- move the reference maximum up and rescale what was accumulated ----
+    const float m_new = fmaxf(m_run, tmax);
+    if (m_run != -INFINITY) {  // on the first tile nothing has been accumulated yet
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] *= alpha;
+    }
+    m_run = m_new;
   }
 
   // ---- normalise and write this chunk's result ----
-  float l_tot = xor_sum(l_run, 16);
-  l_tot = xor_sum(l_tot, 32);
+  const float l_tot = sum_over_token_lanes(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int fb = 0; fb < kDc / 16; ++fb)
-    *reinterpret_cast<float4*>(po + fb * 16 + 4 * g) =
-        make_float4(acc[fb][0] * inv, acc[fb][1] * inv, acc[fb][2] * inv, acc[fb][3] * inv);
+  for (int fb = 0; fb < kDc / 16; ++fb) {
+    const f32x4 v = acc[fb] * inv;
+    *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
   if (g == 0) *pl = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
 }
 
 }  // namespace
 
 hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s) {
-  // more than 64 KB of dynamic LDS has to be requested once per process
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(split_attn_bf16_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (attr != hipSuccess) return attr;
   SplitArgs p;
   p.q_abs = static_cast<const uint16_t*>(a.q_abs);
   p.q_r = static_cast<const uint16_t*>(a.q_r);
@@ -278,7 +416,7 @@ hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s) {
   p.rope_pool = static_cast<const uint16_t*>(a.rope_pool);
   p.page_table = a.page_table;
   p.context_lens = a.context_lens;
-  p.part_o = a.part_o;
+  p.part_o = static_cast<uint16_t*>(a.part_o);
   p.part_lse = a.part_lse;
   p.batch = a.batch;
   p.n_q = a.n_q;
@@ -293,7 +431,7 @@ hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s) {
   p.scale_log2 = a.scale_log2;
   const int units = a.batch * a.splits;
   const int groups = ((units + 7) / 8) * 8 * a.n_q * p.head_groups;
-  hipLaunchKernelGGL(split_attn_bf16_kernel, dim3(groups), dim3(kThreads), kLdsBytes, s, p);
+  hipLaunchKernelGGL(split_attn_bf16_kernel, dim3(groups), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -102,7 +102,7 @@ def test_workspace_size_and_split_plan(L):
             assert (S - 1) * chunk < T <= S * chunk
             ws = binding.mla_decode_workspace_size(plan, B, n_q, T)
             R = B * n_q
-            need = R * S * 128 * 512 * 4 + R * S * 128 * 4 + 2 * R * 128 * 512 * 2
+            need = R * S * 128 * 512 * 2 + R * S * 128 * 4 + 2 * R * 128 * 512 * 2
             assert need <= ws <= need + 4 * 256
         assert binding.mla_decode_workspace_size(plan, 0, 1, 10) == 0
         # invalid shapes give 0 and a reason

@@ -3,45 +3,51 @@
 // For one query row r, one chunk [t0, t1) of the context and a group of
 // 64 heads, computes over the chunk
 //   s_t   = scale * (q_abs . C[t] + q_R . K_R[t])        (score)
-//   p_t   = exp(s_t - m) with the running max m           (online softmax)
+//   p_t   = exp(s_t - m) with a running reference m      (online softmax)
 //   acc   = sum_t p_t C[t],  l = sum_t p_t                (latent accumulation)
 // and writes the chunk's normalised latent acc / l (bf16) and its base-2
-// log-sum-exp (fp32).  The cache is contracted last for the scores and first for
-// the values, which is the cheapest association for a single query ("MLA,
-// dim by dim" section 4.2 and the cached-decode chains of section 5.2; the
-// concatenated content + RoPE dot product of "Mathematical Prerequisites for
-// DeepSeek-V2" section 9; one scale on the summed score as in "From Vanilla
-// Transformers to Modern LLMs ... Part 3" section 3.o).  Per cached token
-// and query row this is 4 h d_c + 2 h d_r + h FLOPs over d_c + d_r cached
-// values ("MLA, dim by dim", FLOPs table of section 5.2).
+// log-sum-exp (fp32).  The cache is contracted last for the scores and
+// first for the values, which is the cheapest association for a single
+// query ("MLA, dim by dim" section 4.2 and the cached-decode chains of
+// section 5.2; the concatenated content + RoPE dot product of "Mathematical
+// Prerequisites for DeepSeek-V2" section 9; one scale on the summed score as
+// in "From Vanilla Transformers to Modern LLMs ... Part 3" section 3.o).
+// Per cached token and query row this is 4 h d_c + 2 h d_r + h FLOPs over
+// d_c + d_r cached values ("MLA, dim by dim", FLOPs table of section 5.2).
 //
 // gfx950 design
-// - 256 threads = 4 wave64s, 16 heads per wave, one work-group per CU (the
-//   fp32 accumulator and the bf16 query need most of the 512-entry register
-//   file of one wave per SIMD).
-// - The chunk is streamed in 32-token tiles through a ring of four LDS
-//   stages filled by direct global->LDS DMA (global_load_lds_dwordx4): no
-//   registers are spent on staging and three tiles are in flight while a
-//   fourth is consumed.  A tile never straddles a cache page (pages are multiples of
-//   32 tokens), so each tile is one contiguous run of 32 latent rows and 32
-//   RoPE rows in the pool; the pool row of every tile is looked up once at
-//   the start.  Every latent row is read from HBM once per work-group with
-//   1 KB per instruction, and all 64 heads of the group reuse it from LDS.
+// - 512 threads = 8 wave64s, two per SIMD, in two roles over the same four
+//   16-head blocks:
+//     score waves (0-3): issue the tile DMAs, compute the scores of tile k,
+//       run the online softmax and publish the bf16 probabilities P(k) to
+//       LDS (plus per-head rescale factors when the reference maximum moves);
+//     accumulate waves (4-7): fold P(k-1) into the fp32 latent accumulator
+//       (64 heads x 512 features, in MFMA registers) against tile k-1.
+//   Each SIMD runs one wave of each role, so the LDS latency of one role is
+//   covered by the MFMAs of the other, and each role fits in 256 registers.
+//   One work-group barrier per tile orders everything.
+// - The chunk streams in 32-token tiles through a ring of four LDS stages
+//   filled by direct global->LDS DMA (global_load_lds_dwordx4): no staging
+//   registers; tiles k+1 and k+2 are in flight while the score waves read
+//   tile k and the accumulate waves read tile k-1.  A tile never straddles a
+//   cache page (pages are multiples of 32 tokens), so each tile is one
+//   contiguous run of 32 latent rows and 32 RoPE rows in the pool; every
+//   tile's pool row is looked up once at the start.
 // - The tile stays token-major in LDS with its 16-byte chunks XOR-swizzled
 //   per row, so that both read patterns below are free of bank conflicts.
 // - Scores: S^T[token][head] = KV[token][:] . Q[head][:] on 16x16x32 bf16
 //   MFMA, tokens as M, heads as N, K over the 576 latent + RoPE features.
-//   The absorbed query (bf16) stays in registers for the whole chunk.
-// - With heads as N each lane holds one head's scores for 8 tokens, so the
-//   running max and the rescale of the accumulator are per-lane values; the
-//   tile maximum needs two cross-lane steps.
+//   The absorbed query (bf16) stays in registers for the whole chunk.  With
+//   heads as N each lane holds one head's scores for 8 tokens, so softmax
+//   state is per lane and the tile maximum needs two cross-lane swaps.
 // - Latent accumulation: O^T[feature][head] += C^T[feature][token] .
 //   P^T[token][head], features as M (32 blocks of 16), heads as N, tokens as
 //   K.  The feature-major A operand comes straight from the token-major tile
 //   through the transposing LDS read ds_read_b64_tr_b16 (within 16 lanes,
 //   lane i receives element i & 3 of the 8-byte chunk addressed by lane
-//   4e + (i >> 2), for e = 0..3).  The probabilities come out of the score
-//   accumulators already in the matching B-operand order.
+//   4e + (i >> 2), for e = 0..3).  P comes out of the score accumulators
+//   already in the matching B-operand order, so it crosses LDS as one
+//   16-byte store and load per lane.
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.
@@ -55,21 +61,36 @@ namespace {
 constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kDkv = kDc + kDr;
-constexpr int kTile = kFastTile;          // 32 tokens
-constexpr int kWaves = kFastHeadsPerGroup / 16;
-constexpr int kThreads = 64 * kWaves;     // 256
-constexpr int kStages = 4;                // LDS ring depth (three tiles in flight)
-constexpr int kLatBytes = kTile * kDc * 2;    // 32 KB: 32 rows of 1 KB
-constexpr int kRopeBytes = kTile * kDr * 2;   // 4 KB: 32 rows of 128 B
+constexpr int kTile = kFastTile;                  // 32 tokens
+constexpr int kBlocks = kFastHeadsPerGroup / 16;  // 16-head blocks per group (4)
+constexpr int kThreads = 2 * 64 * kBlocks;        // one score + one accumulate wave per block
+constexpr int kStages = 4;                        // LDS ring depth
+constexpr int kLatBytes = kTile * kDc * 2;        // 32 KB: 32 rows of 1 KB
+constexpr int kRopeBytes = kTile * kDr * 2;       // 4 KB: 32 rows of 128 B
 constexpr int kStageBytes = kLatBytes + kRopeBytes;
 
-static_assert(kThreads == 256 && kTile == 32, "load mapping assumes 4 waves and 32-token tiles");
+static_assert(kThreads == 512 && kTile == 32, "load mapping assumes 4 blocks and 32-token tiles");
 // Largest factor (as a power of two) by which a weight may exceed 1 before
 // the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
 constexpr float kRescaleSlack = 8.0f;
 
 #define AS3 __attribute__((address_space(3)))
 typedef short tr_vec __attribute__((vector_size(8)));  // operand type of the transposing read
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+struct SplitArgs {
+  const uint16_t* q_abs;        // [R][h][512]
+  const uint16_t* q_r;          // [R][h][64]
+  const uint16_t* latent_pool;  // [P][page][512]
+  const uint16_t* rope_pool;    // [P][page][64]
+  const int32_t* page_table;    // [B][max_pages]
+  const int32_t* context_lens;  // [B]
+  uint16_t* part_o;             // [R][S][h][512] bf16
+  float* part_lse;              // [R][S][h]
+  int batch, n_q, h, head_groups, splits, chunk_len;
+  int page_size, max_pages, num_pages, max_len;
+  float scale_log2;
+};
 
 // Swizzle of the 16-byte chunk index within latent row r of a tile (only
 // r mod 16 matters).  Chosen so that the score operand reads (16 rows, one
@@ -118,30 +139,27 @@ __device__ __forceinline__ float sum_over_token_lanes(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Work-group barrier that orders LDS accesses (this wave's LDS stores have
+// completed) but leaves outstanding global->LDS DMAs alone: those are waited
+// for explicitly with vmcnt, so the next tiles stay in flight across it.
 __device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-struct SplitArgs {
-  const uint16_t* q_abs;        // [R][h][512]
-  const uint16_t* q_r;          // [R][h][64]
-  const uint16_t* latent_pool;  // [P][page][512]
-  const uint16_t* rope_pool;    // [P][page][64]
-  const int32_t* page_table;    // [B][max_pages]
-  const int32_t* context_lens;  // [B]
-  uint16_t* part_o;             // [R][S][h][512] bf16
-  float* part_lse;              // [R][S][h]
-  int batch, n_q, h, head_groups, splits, chunk_len;
-  int page_size, max_pages, num_pages, max_len;
-  float scale_log2;
+struct Shared {
+  uint8_t ring[kStages * kStageBytes];  // the tile ring (token-major, swizzled)
+  u32x4 prob[2][kBlocks][64];           // P(k) per 16-head block, in B-operand order
+  float alpha[2][kBlocks * 16];         // rescale factor per head when flagged
+  int rescale[2][kBlocks];              // per block: accumulator must be rescaled
+  float inv_l[kBlocks * 16];            // 1 / sum of weights, per head, at the end
+  int tile_row[kMaxFastChunkTiles];     // pool row of each tile's first token
 };
-
+static_assert(sizeof(Shared) <= 160 * 1024, "LDS budget");
 
 __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t ring[kStages * kStageBytes];
-  __shared__ int tile_row[kMaxFastChunkTiles];
+  __shared__ __attribute__((aligned(16))) Shared sh;
 
   // ---- which (sequence, chunk, query token, head group) this group owns ----
   const int sharers = p.n_q * p.head_groups;
@@ -162,40 +180,38 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   const int t1 = min(t0 + p.chunk_len, vis);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
-  const int head = hgi * kFastHeadsPerGroup + 16 * wave + l16;
+  const bool scorer = wave < kBlocks;
+  const int hb = wave & (kBlocks - 1);  // 16-head block of this wave
+  const int head = hgi * kFastHeadsPerGroup + 16 * hb + l16;
 
   uint16_t* po = p.part_o + (((size_t)r * p.splits + split) * p.h + head) * kDc;
   float* pl = p.part_lse + ((size_t)r * p.splits + split) * p.h + head;
 
   if (t0 >= t1) {  // nothing visible in this chunk for this query row
+    if (scorer) {
+      if (g == 0) *pl = -INFINITY;
+    } else {
 #pragma unroll 4
-    for (int fb = 0; fb < kDc / 16; ++fb) *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) = make_uint2(0, 0);
-    if (g == 0) *pl = -INFINITY;
+      for (int fb = 0; fb < kDc / 16; ++fb) *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) = make_uint2(0, 0);
+    }
     return;
   }
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;  // <= kMaxFastChunkTiles (host-checked)
+  const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)sh.ring);
 
-  f32x4 acc[kDc / 16];
-#pragma unroll
-  for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)ring);
-  static_assert(kStages * kStageBytes + kMaxFastChunkTiles * 4 <= 160 * 1024, "LDS budget");
-
-  // Tile i -> stage i % kStages: wave w copies latent rows 8w..8w+7 (one
-  // 1 KB row per DMA) and RoPE rows 8w..8w+7 (one DMA); row0 is the pool row
-  // of the tile's first token.  Rows past the end of the chunk repeat the
-  // tile's first row, so the LDS never holds non-finite garbage; their
-  // probabilities are exactly 0.  Exactly 9 DMAs per wave per tile; all
-  // address arithmetic is scalar except the per-lane offsets fixed here.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Tile i -> stage i % kStages.  Score wave w copies latent rows 8w..8w+7
+  // (one 1 KB row per DMA) and RoPE rows 8w..8w+7 (one DMA); row0 is the
+  // pool row of the tile's first token.  Rows past the end of the chunk
+  // repeat the tile's first row, so the LDS never holds non-finite garbage;
+  // their probabilities are exactly 0.  Exactly 9 DMAs per score wave per
+  // tile; all address arithmetic is scalar except the lane offsets below.
   uint32_t lat_voff[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(8 * wave_u + j));
-  const int rope_row = 8 * wave_u + (lane >> 3);
+  for (int j = 0; j < 8; ++j) lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(8 * hb + j));
+  const int rope_row = 8 * hb + (lane >> 3);
   const uint32_t rope_chunk = 16u * (uint32_t)((lane & 7) ^ rope_swz(rope_row));
   const uint32_t rope_voff = (uint32_t)rope_row * (kDr * 2) + rope_chunk;
   auto issue = [&](int i, int row0) {
@@ -205,12 +221,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     const uint8_t* lat_tile = reinterpret_cast<const uint8_t*>(p.latent_pool) + (size_t)row0 * (kDc * 2);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int rr = 8 * wave_u + j;
+      const int rr = 8 * hb + j;
       lds_dma16(lat_tile + (rr < nvalid ? rr : 0) * (kDc * 2), lat_voff[j], sb + rr * (kDc * 2));
     }
     const uint8_t* rope_tile = reinterpret_cast<const uint8_t*>(p.rope_pool) + (size_t)row0 * (kDr * 2);
     const uint32_t voff = nvalid == kTile ? rope_voff : (rope_row < nvalid ? rope_voff : rope_chunk);
-    lds_dma16(rope_tile, voff, sb + kLatBytes + 8 * wave_u * (kDr * 2));
+    lds_dma16(rope_tile, voff, sb + kLatBytes + 8 * hb * (kDr * 2));
   };
   auto tile_pool_row = [&](int i) {
     const int ts = t0 + i * kTile;
@@ -219,159 +235,190 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     return pg * p.page_size + ts % p.page_size;
   };
 
-  // ---- prologue, ordered to shorten the chain of HBM latencies: the first
-  //      tiles' page lookups and DMAs go out first, then the query loads,
-  //      then the page lookups of the remaining tiles ----
-  {
-    // all lookups first (one wait), then the DMAs
-    int row[kStages - 1];
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i) row[i] = i < ntiles ? tile_pool_row(i) : 0;
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-      if (i < ntiles) issue(i, row[i]);
-  }
+  auto fill_tile_rows = [&]() {
+    for (int i = 2 + tid; i < ntiles; i += kThreads) sh.tile_row[i] = tile_pool_row(i);
+  };
 
-  bf16x8 qa[kDc / 32], qr[kDr / 32];
-  {
-    const uint16_t* qa_row = p.q_abs + ((size_t)r * p.h + head) * kDc;
-    const uint16_t* qr_row = p.q_r + ((size_t)r * p.h + head) * kDr;
-#pragma unroll
-    for (int s = 0; s < kDc / 32; ++s)
-      qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qa_row + 32 * s + 8 * g));
-#pragma unroll
-    for (int s = 0; s < kDr / 32; ++s)
-      qr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr_row + 32 * s + 8 * g));
-  }
-  for (int i = kStages - 1 + tid; i < ntiles; i += kThreads) tile_row[i] = tile_pool_row(i);
-  // Consume the query registers here: waiting for them also drains the
-  // prologue DMAs (older in the same counter), after which the ring's vmcnt
-  // bookkeeping owns the counter.
-#pragma unroll
-  for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
-#pragma unroll
-  for (int s = 0; s < kDr / 32; ++s) asm volatile("" :: "v"(qr[s]));
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // tile_row is visible, the first tiles are in LDS
-
-  // Per-lane LDS byte offsets of the two read patterns within a stage; the
-  // remaining parts of every address are compile-time immediates.
+  // Per-lane LDS byte offsets of the two read patterns within a stage:
   //  score reads: row l16 (+16 tb), chunk 4s + g -> (4s) ^ c1_x with
   //               c1_x = g ^ lat_swz(l16) < 16, i.e. base[s & 3] + 256 (s >> 2)
   //  transposing reads: row 4g + e (+16 tb), chunk 2 fb + (q >> 1), half q & 1
   //               -> base[fb & 7] + 256 (fb >> 3)
-  const int c1_x = g ^ lat_swz(l16);
-  const int rope_x = g ^ rope_swz(l16);
-  const int tr_row = 4 * g + (l16 >> 2);
-  const int tr_x = ((l16 & 3) >> 1) ^ lat_swz(tr_row);
-  uint32_t c1_base[4], rope_base[2], tr_base[8];
+  // Each role keeps all of its state inside its own branch, so that nothing
+  // of one role is live across the other's loop.
+  // Iteration it (0..ntiles): score waves handle tile it, accumulate waves
+  // tile it - 1; both roles pass the same ntiles + 1 barriers.  P(k) and the
+  // rescale flags of tile k live in slot k & 1: written by the score waves
+  // between barriers k and k + 1, read by the accumulate waves between
+  // barriers k + 1 and k + 2, and overwritten (tile k + 2) only after that.
+  if (scorer) {
+    // ---- prologue: the first two tiles' lookups and DMAs go out first, then
+    //      the query loads, then the lookups of the remaining tiles ----
+    bf16x8 qa[kDc / 32], qr[kDr / 32];
+    {
+      const int row_a = tile_pool_row(0);
+      const int row_b = ntiles > 1 ? tile_pool_row(1) : 0;
+      issue(0, row_a);
+      if (ntiles > 1) issue(1, row_b);
+      const uint16_t* qa_row = p.q_abs + ((size_t)r * p.h + head) * kDc;
+      const uint16_t* qr_row = p.q_r + ((size_t)r * p.h + head) * kDr;
 #pragma unroll
-  for (int k2 = 0; k2 < 4; ++k2) c1_base[k2] = l16 * (kDc * 2) + 16 * ((4 * k2) ^ c1_x);
+      for (int s = 0; s < kDc / 32; ++s)
+        qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qa_row + 32 * s + 8 * g));
 #pragma unroll
-  for (int k2 = 0; k2 < 2; ++k2) rope_base[k2] = kLatBytes + l16 * (kDr * 2) + 16 * ((4 * k2) ^ rope_x);
+      for (int s = 0; s < kDr / 32; ++s)
+        qr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr_row + 32 * s + 8 * g));
+    }
+    fill_tile_rows();
+    // Consume the query registers here: waiting for them also drains the
+    // prologue DMAs (older in the same counter), after which the ring's
+    // vmcnt bookkeeping owns the counter.
 #pragma unroll
-  for (int k2 = 0; k2 < 8; ++k2)
-    tr_base[k2] = tr_row * (kDc * 2) + 16 * ((2 * k2) ^ tr_x) + 8 * (l16 & 1);
+    for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
+#pragma unroll
+    for (int s = 0; s < kDr / 32; ++s) asm volatile("" :: "v"(qr[s]));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile_row is visible, the first tiles are in LDS
 
-  // The rescale of the accumulator (rare: the reference maximum only moves
-  // when a score exceeds it by more than kRescaleSlack) lives outside the
-  // inner tile loop, which breaks out to it and then resumes at the same
-  // tile, recomputing its scores.  Keeping every VALU use of the
-  // accumulator out of the hot loop lets it stay in the MFMA registers.
-  int it = 0;
-  bool arrived = false;  // tile `it` already waited for and its successor issued
-  float tmax = -INFINITY;
-  while (it < ntiles) {
-    for (; it < ntiles; ++it) {
-      const int ts = t0 + it * kTile;
-      if (!arrived) {
-        // Tile `it` has landed once only the DMAs of the tiles after it (9
-        // per tile per wave, at most kStages - 2 tiles) are pending.
-        static_assert(kStages == 4, "the waits below count DMAs for a four-stage ring");
-        const int ahead = ntiles - 1 - it;
-        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    const int c1_x = g ^ lat_swz(l16);
+    const int rope_x = g ^ rope_swz(l16);
+    uint32_t c1_base[4], rope_base[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) c1_base[k2] = l16 * (kDc * 2) + 16 * ((4 * k2) ^ c1_x);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) rope_base[k2] = kLatBytes + l16 * (kDr * 2) + 16 * ((4 * k2) ^ rope_x);
+
+    float m_run = -INFINITY, l_run = 0.f;  // reference maximum, per-lane partial weight sum
+    for (int it = 0; it <= ntiles; ++it) {
+      if (it < ntiles) {
+        // tile `it` has landed once only the next tile's 9 DMAs are pending
+        if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
         else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        block_barrier();  // every wave's part of tile `it` is in LDS, tile it-1 is consumed
-        if (it + kStages - 1 < ntiles) issue(it + kStages - 1, tile_row[it + kStages - 1]);
       }
-      arrived = false;
+      block_barrier();
+      if (it >= ntiles) continue;
+        const int ts = t0 + it * kTile;
+        if (it + 2 < ntiles) issue(it + 2, sh.tile_row[it + 2]);
+        const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (it % kStages) * kStageBytes;
 
-      const AS3 uint8_t* stage = (const AS3 uint8_t*)ring + (it % kStages) * kStageBytes;
-
-    // ---- scores: S^T[tb*16 + 4g + j][head]; operands prefetched one step ahead ----
-    auto score_operand = [&](int s, int tb) -> bf16x8 {
-      const AS3 uint8_t* src = s < kDc / 32
-          ? stage + c1_base[s & 3] + 256 * (s >> 2) + tb * 16 * (kDc * 2)
-          : stage + rope_base[s - kDc / 32] + tb * 16 * (kDr * 2);
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(src));
-    };
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
-      bf16x8 cur0 = score_operand(0, 0), cur1 = score_operand(0, 1);
+        // ---- scores: S^T[tb*16 + 4g + j][head], operands three steps ahead ----
+        auto score_operand = [&](int s, int tb) -> bf16x8 {
+          const AS3 uint8_t* src = s < kDc / 32
+              ? stage + c1_base[s & 3] + 256 * (s >> 2) + tb * 16 * (kDc * 2)
+              : stage + rope_base[s - kDc / 32] + tb * 16 * (kDr * 2);
+          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(src));
+        };
+        constexpr int kAhead = 3;
+        constexpr int kSteps = kDkv / 32;
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        bf16x8 opq[kAhead + 1][2];
 #pragma unroll
-      for (int s = 0; s < kDkv / 32; ++s) {
-        bf16x8 nxt0 = cur0, nxt1 = cur1;
-        if (s + 1 < kDkv / 32) {
-          nxt0 = score_operand(s + 1, 0);
-          nxt1 = score_operand(s + 1, 1);
+        for (int s = 0; s < kAhead; ++s) {
+          opq[s][0] = score_operand(s, 0);
+          opq[s][1] = score_operand(s, 1);
         }
-        const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
-        sacc[0] = mfma16x16x32(cur0, bq, sacc[0]);
-        sacc[1] = mfma16x16x32(cur1, bq, sacc[1]);
-        cur0 = nxt0;
-        cur1 = nxt1;
-      }
-    }
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          if (s + kAhead < kSteps) {
+            opq[(s + kAhead) % (kAhead + 1)][0] = score_operand(s + kAhead, 0);
+            opq[(s + kAhead) % (kAhead + 1)][1] = score_operand(s + kAhead, 1);
+          }
+          const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
+          sacc[0] = mfma16x16x32(opq[s % (kAhead + 1)][0], bq, sacc[0]);
+          sacc[1] = mfma16x16x32(opq[s % (kAhead + 1)][1], bq, sacc[1]);
+        }
 
-    // ---- online softmax (base 2), per lane = per head ----
-    // m_run is a reference maximum, not necessarily the exact running max;
-    // the final division by l_run makes the result independent of it.
-    // Scores stay unscaled until the exponent (scale > 0, so maxima commute).
-    if (ts + kTile > t1) {  // the chunk's last tile: tokens past t1 weigh 0
+        // ---- online softmax (base 2), per lane = per head ----
+        // m_run is a reference maximum, not necessarily the exact running
+        // max: it moves only when a score exceeds it by more than
+        // kRescaleSlack, so weights stay below 2^kRescaleSlack and most tiles
+        // need no rescale.  The final division by l makes the result
+        // independent of the reference.  Scores stay unscaled until the
+        // exponent (scale > 0, so maxima commute with it).
+        if (ts + kTile > t1) {  // the chunk's last tile: tokens past t1 weigh 0
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+          for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (ts + tb * 16 + 4 * g + j >= t1) sacc[tb][j] = -INFINITY;
+            for (int j = 0; j < 4; ++j)
+              if (ts + tb * 16 + 4 * g + j >= t1) sacc[tb][j] = -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                           fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+        tmax = max_over_token_lanes(tmax) * p.scale_log2;
+        const int slot = it & 1;
+        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
+          const float m_new = fmaxf(m_run, tmax);
+          // nothing has been accumulated before the first tile: no rescale
+          const int flag = m_run != -INFINITY;
+          if (flag) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            if (g == 0) sh.alpha[slot][16 * hb + l16] = alpha;
+          }
+          if (lane == 0) sh.rescale[slot][hb] = flag;
+          m_run = m_new;
+        } else if (lane == 0) {
+          sh.rescale[slot][hb] = 0;
+        }
+        f32x8 pf;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            pf[tb * 4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][j], p.scale_log2, -m_run));
+        const bf16x8 pb = __builtin_convertvector(pf, bf16x8);  // round to nearest even
+        sh.prob[slot][hb][lane] = __builtin_bit_cast(u32x4, pb);
+        // sum of the weights the MFMA sees (bf16), two per dot2
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 two = {pb[e], pb[e + 1]};
+          psum = __builtin_amdgcn_fdot2_f32_bf16(two, one, psum, false);
+        }
+        l_run += psum;
     }
-    tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                 fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-    tmax = max_over_token_lanes(tmax) * p.scale_log2;
-    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
-      arrived = true;
-      break;  // rescale outside the hot loop, then redo this tile
+    const float l_tot = sum_over_token_lanes(l_run);
+    if (g == 0) {
+      *pl = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+      sh.inv_l[16 * hb + l16] = l_tot > 0.f ? 1.f / l_tot : 0.f;
     }
-    f32x8 pf;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        pf[tb * 4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][j], p.scale_log2, -m_run));
-    const bf16x8 pb = __builtin_convertvector(pf, bf16x8);  // round to nearest even
-    {
-      // sum of the weights the MFMA sees (bf16), two per dot2
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 two = {pb[e], pb[e + 1]};
-        psum = __builtin_amdgcn_fdot2_f32_bf16(two, one, psum, false);
-      }
-      l_run += psum;
-    }
+  } else {
+    fill_tile_rows();
+    __syncthreads();  // pairs with the score waves' prologue barrier
 
-    // ---- latent accumulation: O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
-    auto latent_operand = [&](int fb) -> bf16x8 {
-      const AS3 uint8_t* a0 = stage + tr_base[fb & 7] + 256 * (fb >> 3);
-      const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)a0));
-      const u16x4 hi = __builtin_bit_cast(
-          u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)(a0 + 16 * (kDc * 2))));
-      const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      return as_bf16x8(v);
-    };
-    {
+    const int tr_row = 4 * g + (l16 >> 2);
+    const int tr_x = ((l16 & 3) >> 1) ^ lat_swz(tr_row);
+    uint32_t tr_base[8];
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2)
+      tr_base[k2] = tr_row * (kDc * 2) + 16 * ((2 * k2) ^ tr_x) + 8 * (l16 & 1);
+
+    f32x4 acc[kDc / 16];
+#pragma unroll
+    for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it <= ntiles; ++it) {
+      block_barrier();
+      if (it == 0) continue;
+      const int j = it - 1;  // tile folded in this iteration
+      const int slot = j & 1;
+      if (sh.rescale[slot][hb] != 0) {  // the reference maximum moved
+        const float alpha = sh.alpha[slot][16 * hb + l16];
+#pragma unroll
+        for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] *= alpha;
+      }
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, sh.prob[slot][hb][lane]);
+      const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (j % kStages) * kStageBytes;
+
+      // ---- latent accumulation: O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
+      auto latent_operand = [&](int fb) -> bf16x8 {
+        const AS3 uint8_t* a0 = stage + tr_base[fb & 7] + 256 * (fb >> 3);
+        const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)a0));
+        const u16x4 hi = __builtin_bit_cast(
+            u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)(a0 + 16 * (kDc * 2))));
+        const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return as_bf16x8(v);
+      };
       bf16x8 cur = latent_operand(0);
 #pragma unroll
       for (int fb = 0; fb < kDc / 16; ++fb) {
@@ -381,29 +428,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
         cur = nxt;
       }
     }
-    }
-    if (it >= ntiles) break;
-    // ---- move the reference maximum up and rescale what was accumulated ----
-    const float m_new = fmaxf(m_run, tmax);
-    if (m_run != -INFINITY) {  // on the first tile nothing has been accumulated yet
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    __syncthreads();  // inv_l is visible
+    const float inv = sh.inv_l[16 * hb + l16];
 #pragma unroll
-      for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] *= alpha;
+    for (int fb = 0; fb < kDc / 16; ++fb) {
+      const f32x4 v = acc[fb] * inv;
+      *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
-    m_run = m_new;
+    return;
   }
-
-  // ---- normalise and write this chunk's result ----
-  const float l_tot = sum_over_token_lanes(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-#pragma unroll
-  for (int fb = 0; fb < kDc / 16; ++fb) {
-    const f32x4 v = acc[fb] * inv;
-    *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) =
-        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-  }
-  if (g == 0) *pl = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+  __syncthreads();  // pairs with the accumulate waves' barrier above
 }
 
 }  // namespace

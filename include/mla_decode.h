@@ -128,9 +128,11 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing (instrumentation, off by default).  With max_runs > 0
- * every later `run` on this plan also records HIP events before and after
- * each of its four kernels (absorb, split, combine, up-project) on the
- * caller's stream, for up to max_runs runs; max_runs = 0 turns it off.
+ * every later `run` on this plan launches each of its four kernels (absorb,
+ * split, combine, up-project) with a start and a stop HIP event that the
+ * dispatch itself fills in (the kernel's own begin and end, as a profiler
+ * sees them, not the gaps between launches), for up to max_runs runs;
+ * max_runs = 0 turns it off.
  * Creates the events on the current device; allocates no device memory. */
 mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs);
 

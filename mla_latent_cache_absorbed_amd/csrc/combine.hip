@@ -104,14 +104,14 @@ __global__ __launch_bounds__(256) void combine_fast_kernel(const uint16_t* __res
 
 }  // namespace
 
-hipError_t launch_combine(const DecodeArgs& a, bool fast, hipStream_t s) {
+hipError_t launch_combine(const DecodeArgs& a, bool fast, const LaunchCtx& s) {
   const int blocks = a.batch * a.n_q * a.h;
   if (fast)
-    hipLaunchKernelGGL(combine_fast_kernel, dim3(blocks, 2), dim3(256), 0, s,
+    launch_kernel(combine_fast_kernel, dim3(blocks, 2), dim3(256), s,
                        static_cast<const uint16_t*>(a.part_o), a.part_lse,
                        static_cast<uint16_t*>(a.c_bar), a.splits, a.h);
   else
-    hipLaunchKernelGGL(combine_general_kernel<false>, dim3(blocks), dim3(128), 0, s,
+    launch_kernel(combine_general_kernel<false>, dim3(blocks), dim3(128), s,
                        static_cast<const float*>(a.part_o), a.part_lse, a.c_bar, a.splits, a.h,
                        a.d_c);
   return hipGetLastError();

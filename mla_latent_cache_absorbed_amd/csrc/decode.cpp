@@ -18,6 +18,7 @@
 #include "kernels.h"
 
 constexpr int kKernels = 4;  // absorb, split, combine, up-project
+constexpr int kEventsPerRun = 2 * kKernels;
 
 struct mla_decode_plan {
   mla_decode_config_t cfg;
@@ -25,7 +26,8 @@ struct mla_decode_plan {
   bool fast;       // bf16 MFMA kernels apply
   float scale;     // resolved softmax scale
   int num_cus;     // compute units the split heuristic fills
-  // optional per-kernel timing: (kKernels + 1) events per recorded run
+  // optional per-kernel timing: a start and a stop event per kernel per
+  // recorded run, filled in by the launches themselves
   std::vector<hipEvent_t> events;
   int timing_capacity = 0;
   int timing_runs = 0;
@@ -269,22 +271,22 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = nullptr;
   if (plan->timing_runs < plan->timing_capacity)
-    ev = &plan->events[(size_t)plan->timing_runs++ * (kKernels + 1)];
+    ev = &plan->events[(size_t)plan->timing_runs++ * kEventsPerRun];
   for (int k = 0; k < kKernels; ++k) {
+    mla::LaunchCtx c;
+    c.stream = hs;
+    if (ev) {
+      c.start = ev[2 * k];
+      c.stop = ev[2 * k + 1];
+    }
     hipError_t e;
-    if (ev && (e = hipEventRecord(ev[k], hs)) != hipSuccess)
-      return fail(MLA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
     switch (k) {
-      case 0: e = p.fast ? mla::launch_q_absorb_bf16(a, hs) : mla::launch_q_absorb_general(a, hs); break;
-      case 1: e = p.fast ? mla::launch_split_attn_bf16(a, hs) : mla::launch_split_attn_general(a, hs); break;
-      case 2: e = mla::launch_combine(a, p.fast, hs); break;
-      default: e = p.fast ? mla::launch_up_project_bf16(a, hs) : mla::launch_up_project_general(a, hs); break;
+      case 0: e = p.fast ? mla::launch_q_absorb_bf16(a, c) : mla::launch_q_absorb_general(a, c); break;
+      case 1: e = p.fast ? mla::launch_split_attn_bf16(a, c) : mla::launch_split_attn_general(a, c); break;
+      case 2: e = mla::launch_combine(a, p.fast, c); break;
+      default: e = p.fast ? mla::launch_up_project_bf16(a, c) : mla::launch_up_project_general(a, c); break;
     }
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  }
-  if (ev) {
-    hipError_t e = hipEventRecord(ev[kKernels], hs);
-    if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   }
   return MLA_OK;
 }
@@ -298,7 +300,7 @@ mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs) {
   plan->events.clear();
   plan->timing_capacity = 0;
   plan->timing_runs = 0;
-  const size_t n = (size_t)max_runs * (kKernels + 1);
+  const size_t n = (size_t)max_runs * kEventsPerRun;
   plan->events.reserve(n);
   for (size_t i = 0; i < n; ++i) {
     hipEvent_t e;
@@ -320,14 +322,14 @@ mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs)
   for (int k = 0; k < kKernels; ++k) ms[k] = 0.f;
   const int n = plan->timing_runs;
   if (n > 0) {
-    hipError_t st = hipEventSynchronize(plan->events[(size_t)n * (kKernels + 1) - 1]);
+    hipError_t st = hipEventSynchronize(plan->events[(size_t)n * kEventsPerRun - 1]);
     if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(st));
   }
   for (int r = 0; r < n; ++r) {
-    const hipEvent_t* ev = &plan->events[(size_t)r * (kKernels + 1)];
+    const hipEvent_t* ev = &plan->events[(size_t)r * kEventsPerRun];
     for (int k = 0; k < kKernels; ++k) {
       float t = 0.f;
-      hipError_t st = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
+      hipError_t st = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
       if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(st));
       ms[k] += t;
     }

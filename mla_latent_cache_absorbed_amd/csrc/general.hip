@@ -119,30 +119,30 @@ inline unsigned blocks_for(size_t n, unsigned per) { return (unsigned)((n + per 
 
 }  // namespace
 
-hipError_t launch_q_absorb_general(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_q_absorb_general(const DecodeArgs& a, const LaunchCtx& s) {
   const int rows = a.batch * a.n_q;
   const size_t n = (size_t)rows * a.h * a.d_c;
   if (a.in_bf16)
-    hipLaunchKernelGGL(absorb_general_kernel<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+    launch_kernel(absorb_general_kernel<uint16_t>, dim3(blocks_for(n, 256)), dim3(256), s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.w_uk),
                        static_cast<float*>(a.q_abs), rows, a.h, a.d_c, a.d_h);
   else
-    hipLaunchKernelGGL(absorb_general_kernel<float>, dim3(blocks_for(n, 256)), dim3(256), 0, s,
+    launch_kernel(absorb_general_kernel<float>, dim3(blocks_for(n, 256)), dim3(256), s,
                        static_cast<const float*>(a.q), static_cast<const float*>(a.w_uk),
                        static_cast<float*>(a.q_abs), rows, a.h, a.d_c, a.d_h);
   return hipGetLastError();
 }
 
-hipError_t launch_split_attn_general(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_split_attn_general(const DecodeArgs& a, const LaunchCtx& s) {
   dim3 grid(a.splits, a.h, a.batch * a.n_q);
   if (a.in_bf16)
-    hipLaunchKernelGGL(split_general_kernel<uint16_t>, grid, dim3(64), 0, s, a);
+    launch_kernel(split_general_kernel<uint16_t>, grid, dim3(64), s, a);
   else
-    hipLaunchKernelGGL(split_general_kernel<float>, grid, dim3(64), 0, s, a);
+    launch_kernel(split_general_kernel<float>, grid, dim3(64), s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_up_project_general(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_up_project_general(const DecodeArgs& a, const LaunchCtx& s) {
   const int rows = a.batch * a.n_q;
   const size_t n = (size_t)rows * a.h * a.d_h;
   const dim3 grid(blocks_for(n, 256)), block(256);
@@ -150,18 +150,18 @@ hipError_t launch_up_project_general(const DecodeArgs& a, hipStream_t s) {
   if (a.in_bf16) {
     const uint16_t* w = static_cast<const uint16_t*>(a.w_uv);
     if (a.out_bf16)
-      hipLaunchKernelGGL((up_general_kernel<uint16_t, uint16_t>), grid, block, 0, s, w, cb,
+      launch_kernel((up_general_kernel<uint16_t, uint16_t>), grid, block, s, w, cb,
                          static_cast<uint16_t*>(a.out), rows, a.h, a.d_c, a.d_h);
     else
-      hipLaunchKernelGGL((up_general_kernel<uint16_t, float>), grid, block, 0, s, w, cb,
+      launch_kernel((up_general_kernel<uint16_t, float>), grid, block, s, w, cb,
                          static_cast<float*>(a.out), rows, a.h, a.d_c, a.d_h);
   } else {
     const float* w = static_cast<const float*>(a.w_uv);
     if (a.out_bf16)
-      hipLaunchKernelGGL((up_general_kernel<float, uint16_t>), grid, block, 0, s, w, cb,
+      launch_kernel((up_general_kernel<float, uint16_t>), grid, block, s, w, cb,
                          static_cast<uint16_t*>(a.out), rows, a.h, a.d_c, a.d_h);
     else
-      hipLaunchKernelGGL((up_general_kernel<float, float>), grid, block, 0, s, w, cb,
+      launch_kernel((up_general_kernel<float, float>), grid, block, s, w, cb,
                          static_cast<float*>(a.out), rows, a.h, a.d_c, a.d_h);
   }
   return hipGetLastError();

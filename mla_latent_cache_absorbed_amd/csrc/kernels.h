@@ -2,6 +2,7 @@
 // gfx950 kernels.  Not part of the public C ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -36,6 +37,23 @@ struct DecodeArgs {
   void* c_bar;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
 };
 
+// Where a kernel is launched.  With both events set, the launch records
+// the kernel's own start and end (the dispatch's timestamps) into them, so
+// that per-kernel times exclude the gaps between launches.
+struct LaunchCtx {
+  hipStream_t stream = nullptr;
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename Kernel, typename... Args>
+inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, const LaunchCtx& c, Args... args) {
+  if (c.start && c.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, c.stream, c.start, c.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, c.stream, args...);
+}
+
 // Heads handled by one work-group of the fast split kernel.
 constexpr int kFastHeadsPerGroup = 64;
 // Tokens staged per LDS tile in the fast split kernel.
@@ -46,17 +64,17 @@ constexpr int kMaxFastChunkTiles = 1024;
 
 // Fast path: bf16 storage, d_c = 512, d_r = 64, d_h = 128, h % 64 == 0,
 // page_size % 32 == 0.
-hipError_t launch_q_absorb_bf16(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_up_project_bf16(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_q_absorb_bf16(const DecodeArgs& a, const LaunchCtx& s);
+hipError_t launch_split_attn_bf16(const DecodeArgs& a, const LaunchCtx& s);
+hipError_t launch_up_project_bf16(const DecodeArgs& a, const LaunchCtx& s);
 
 // General path: any dims (d_c <= 1024), f32 or bf16 storage, f32 math.
-hipError_t launch_q_absorb_general(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_split_attn_general(const DecodeArgs& a, hipStream_t s);
-hipError_t launch_up_project_general(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_q_absorb_general(const DecodeArgs& a, const LaunchCtx& s);
+hipError_t launch_split_attn_general(const DecodeArgs& a, const LaunchCtx& s);
+hipError_t launch_up_project_general(const DecodeArgs& a, const LaunchCtx& s);
 
 // Log-sum-exp merge of the chunk results into c_bar: bf16 partials and
 // c_bar on the fast path, f32 on the general path.
-hipError_t launch_combine(const DecodeArgs& a, bool fast, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs& a, bool fast, const LaunchCtx& s);
 
 }  // namespace mla

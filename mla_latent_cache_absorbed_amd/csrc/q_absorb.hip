@@ -83,10 +83,10 @@ __global__ __launch_bounds__(256) void q_absorb_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_q_absorb_bf16(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_q_absorb_bf16(const DecodeArgs& a, const LaunchCtx& s) {
   const int rows = a.batch * a.n_q;
   dim3 grid(a.h, a.d_c / kCols);
-  hipLaunchKernelGGL(q_absorb_bf16_kernel, grid, dim3(256), 0, s,
+  launch_kernel(q_absorb_bf16_kernel, grid, dim3(256), s,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.w_uk),
                      static_cast<uint16_t*>(a.q_abs), rows, a.h, a.d_c);
   return hipGetLastError();

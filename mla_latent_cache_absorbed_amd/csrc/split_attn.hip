@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
 
 }  // namespace
 
-hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_split_attn_bf16(const DecodeArgs& a, const LaunchCtx& s) {
   SplitArgs p;
   p.q_abs = static_cast<const uint16_t*>(a.q_abs);
   p.q_r = static_cast<const uint16_t*>(a.q_r);
@@ -466,7 +466,7 @@ hipError_t launch_split_attn_bf16(const DecodeArgs& a, hipStream_t s) {
   p.scale_log2 = a.scale_log2;
   const int units = a.batch * a.splits;
   const int groups = ((units + 7) / 8) * 8 * a.n_q * p.head_groups;
-  hipLaunchKernelGGL(split_attn_bf16_kernel, dim3(groups), dim3(kThreads), 0, s, p);
+  launch_kernel(split_attn_bf16_kernel, dim3(groups), dim3(kThreads), s, p);
   return hipGetLastError();
 }
 

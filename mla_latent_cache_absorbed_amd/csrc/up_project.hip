@@ -65,15 +65,15 @@ __global__ __launch_bounds__(256) void up_project_bf16_kernel(const uint16_t* __
 
 }  // namespace
 
-hipError_t launch_up_project_bf16(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_up_project_bf16(const DecodeArgs& a, const LaunchCtx& s) {
   const int rows = a.batch * a.n_q;
   dim3 grid(a.h, kDh / 64);
   if (a.out_bf16)
-    hipLaunchKernelGGL(up_project_bf16_kernel<true>, grid, dim3(256), 0, s,
+    launch_kernel(up_project_bf16_kernel<true>, grid, dim3(256), s,
                        static_cast<const uint16_t*>(a.w_uv), static_cast<const uint16_t*>(a.c_bar),
                        a.out, rows, a.h);
   else
-    hipLaunchKernelGGL(up_project_bf16_kernel<false>, grid, dim3(256), 0, s,
+    launch_kernel(up_project_bf16_kernel<false>, grid, dim3(256), s,
                        static_cast<const uint16_t*>(a.w_uv), static_cast<const uint16_t*>(a.c_bar),
                        a.out, rows, a.h);
   return hipGetLastError();

@@ -1,0 +1,123 @@
+"""Turn rocprofv3 counter output into per-launch HBM traffic figures.
+
+rocprofv3's FETCH_SIZE and WRITE_SIZE counters (KiB per dispatch, summed over
+the L2 channels) are scaled by what the same counters read for a plain
+device-to-device copy of known size, so that the figure is in real bytes.
+The result goes to ``profiles/traffic.json``, keyed by kernel and workload
+and stamped with a digest of the kernel's source: ``bench.py`` reports it as
+``roofline.traffic`` only while the source is unchanged.
+
+Usage (after one counter run each, see the --help text)::
+
+    python -m mla_latent_cache_absorbed_amd.profiling \\
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
+        --copy-bytes N --workload ds2_t4k --command "..."
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mla_latent_cache_absorbed_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# kernel short name -> (substring of the device symbol, its source file)
+KERNELS = {
+    "q_absorb": ("q_absorb", "q_absorb.hip"),
+    "split_attn": ("split_attn", "split_attn.hip"),
+    "combine": ("combine", "combine.hip"),
+    "up_project": ("up_project", "up_project.hip"),
+}
+
+
+def source_digest(kernel: str) -> str:
+    """Digest of the files that determine one kernel's code."""
+    h = hashlib.sha256()
+    for f in (KERNELS[kernel][1], "common.h", "kernels.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_means(path: str, counter: str) -> dict:
+    """Mean value of one counter per kernel symbol over all its dispatches
+    in a rocprofv3 --output-format csv directory (or file)."""
+    files = [path] if os.path.isfile(path) else glob.glob(
+        os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no counter_collection.csv under %s" % path)
+    vals = defaultdict(list)
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") == counter:
+                    vals[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def short_name(symbol: str):
+    for k, (needle, _) in KERNELS.items():
+        if needle in symbol:
+            return k
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--fetch", required=True, help="rocprofv3 output of the FETCH_SIZE run")
+    ap.add_argument("--write", required=True, help="rocprofv3 output of the WRITE_SIZE run")
+    ap.add_argument("--copy-fetch", required=True, help="FETCH_SIZE run of bench.py --copy-calibration")
+    ap.add_argument("--copy-write", required=True, help="WRITE_SIZE run of bench.py --copy-calibration")
+    ap.add_argument("--copy-bytes", type=int, required=True, help="bytes read (= written) per copy")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--command", default="", help="the profiled command, recorded verbatim")
+    ap.add_argument("--out", default=TRAFFIC_FILE)
+    args = ap.parse_args()
+
+    cf = counter_means(args.copy_fetch, "FETCH_SIZE")
+    cw = counter_means(args.copy_write, "WRITE_SIZE")
+    copy_kernel = max(cf, key=cf.get)  # the copy dominates that run
+    f_factor = args.copy_bytes / (cf[copy_kernel] * 1024.0)
+    w_factor = args.copy_bytes / (cw[copy_kernel] * 1024.0)
+
+    fetch = counter_means(args.fetch, "FETCH_SIZE")
+    write = counter_means(args.write, "WRITE_SIZE")
+    try:
+        with open(args.out) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    for sym in fetch:
+        k = short_name(sym)
+        if k is None or sym not in write:
+            continue
+        fb = fetch[sym] * 1024.0 * f_factor
+        wb = write[sym] * 1024.0 * w_factor
+        table.setdefault(k, {})[args.workload] = {
+            "source_digest": source_digest(k),
+            "bytes_per_launch": fb + wb,
+            "fetch_bytes": fb,
+            "write_bytes": wb,
+            "fetch_kib_raw": fetch[sym],
+            "write_kib_raw": write[sym],
+            "copy_kernel": copy_kernel,
+            "fetch_factor": f_factor,
+            "write_factor": w_factor,
+            "command": args.command,
+        }
+        print("%-11s %-10s fetch %10.3f MB  write %10.3f MB" % (k, args.workload, fb / 1e6, wb / 1e6))
+    os.makedirs(os.path.dirname(args.out), exist_ok=True)
+    with open(args.out, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print("copy kernel %s: fetch factor %.4f, write factor %.4f" % (copy_kernel, f_factor, w_factor))
+
+
+if __name__ == "__main__":
+    main()

@@ -31,8 +31,9 @@ struct DecodeArgs {
 
   // workspace carve-up
   void* q_abs;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
-  void* part_o;     // [R][S][h][d_c]   chunk results already normalised: bf16
-                    //                  (fast path) or f32 (general path)
+  void* part_o;     // chunk results, already normalised.  Fast path: bf16 in
+                    // the split kernel's register order [R][S][h/16][32][64][4]
+                    // (see combine.hip); general path: f32 [R][S][h][d_c]
   float* part_lse;  // [R][S][h]        f32, base-2 log-sum-exp of each chunk
   void* c_bar;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
 };

@@ -13,41 +13,47 @@
 // Prerequisites for DeepSeek-V2" section 9; one scale on the summed score as
 // in "From Vanilla Transformers to Modern LLMs ... Part 3" section 3.o).
 // Per cached token and query row this is 4 h d_c + 2 h d_r + h FLOPs over
-// d_c + d_r cached values ("MLA, dim by dim", FLOPs table of section 5.2).
+// d_c + d_r cached values ("MLA, dim by dim", FLOPs of section 5.2).
 //
 // gfx950 design
-// - 512 threads = 8 wave64s, two per SIMD, in two roles over the same four
-//   16-head blocks:
-//     score waves (0-3): issue the tile DMAs, compute the scores of tile k,
-//       run the online softmax and publish the bf16 probabilities P(k) to
-//       LDS (plus per-head rescale factors when the reference maximum moves);
-//     accumulate waves (4-7): fold P(k-1) into the fp32 latent accumulator
-//       (64 heads x 512 features, in MFMA registers) against tile k-1.
-//   Each SIMD runs one wave of each role, so the LDS latency of one role is
-//   covered by the MFMAs of the other, and each role fits in 256 registers.
-//   One work-group barrier per tile orders everything.
+// - 512 threads = 8 wave64s, two per SIMD, in two roles:
+//     score waves 0-3 (one 16-head block each): scores of tile k on
+//       16x16x32 bf16 MFMA, the online softmax, and the bf16 probabilities
+//       P(k) published to LDS (plus per-head rescale factors when the
+//       reference moves);
+//     accumulate waves 4-7 (128 latent features each, all 64 heads): fold
+//       P(k-1) into the fp32 latent accumulator against tile k-1; every
+//       latent operand they read feeds four MFMAs, one per head block.
+//   Each SIMD runs one wave of each role, so one role's LDS latency is
+//   covered by the other's MFMAs, and each role fits in 256 registers.  One
+//   work-group barrier per tile orders everything.
 // - The chunk streams in 32-token tiles through a ring of four LDS stages
 //   filled by direct global->LDS DMA (global_load_lds_dwordx4): no staging
 //   registers; tiles k+1 and k+2 are in flight while the score waves read
-//   tile k and the accumulate waves read tile k-1.  A tile never straddles a
+//   tile k and the accumulate waves tile k-1.  A DMA instruction holds its
+//   wave at issue for a while, so all eight waves share the 36 DMAs of a
+//   tile and issue them between their MFMAs.  A tile never straddles a
 //   cache page (pages are multiples of 32 tokens), so each tile is one
 //   contiguous run of 32 latent rows and 32 RoPE rows in the pool; every
-//   tile's pool row is looked up once at the start.
+//   tile's pool row is looked up once at the start, in parallel with the
+//   context length and the query loads.
 // - The tile stays token-major in LDS with its 16-byte chunks XOR-swizzled
 //   per row, so that both read patterns below are free of bank conflicts.
-// - Scores: S^T[token][head] = KV[token][:] . Q[head][:] on 16x16x32 bf16
-//   MFMA, tokens as M, heads as N, K over the 576 latent + RoPE features.
-//   The absorbed query (bf16) stays in registers for the whole chunk.  With
-//   heads as N each lane holds one head's scores for 8 tokens, so softmax
-//   state is per lane and the tile maximum needs two cross-lane swaps.
+// - Scores: S^T[token][head] = KV[token][:] . Q[head][:], tokens as M, heads
+//   as N, K over the 576 latent + RoPE features.  The absorbed query (bf16)
+//   stays in registers for the whole chunk.  With heads as N each lane holds
+//   one head's scores for 8 tokens, so softmax state is per lane and a tile
+//   maximum needs two cross-lane swaps.
 // - Latent accumulation: O^T[feature][head] += C^T[feature][token] .
-//   P^T[token][head], features as M (32 blocks of 16), heads as N, tokens as
-//   K.  The feature-major A operand comes straight from the token-major tile
-//   through the transposing LDS read ds_read_b64_tr_b16 (within 16 lanes,
-//   lane i receives element i & 3 of the 8-byte chunk addressed by lane
-//   4e + (i >> 2), for e = 0..3).  P comes out of the score accumulators
-//   already in the matching B-operand order, so it crosses LDS as one
-//   16-byte store and load per lane.
+//   P^T[token][head], features as M, heads as N, tokens as K.  The
+//   feature-major A operand comes straight from the token-major tile through
+//   the transposing LDS read ds_read_b64_tr_b16 (within 16 lanes, lane i
+//   receives element i & 3 of the 8-byte chunk addressed by lane 4e + (i >> 2),
+//   for e = 0..3).  P comes out of the score accumulators already in the
+//   matching B-operand order, so it crosses LDS as one 16-byte store and load
+//   per lane and head block.
+// - The chunk result is stored in register order (512 contiguous bytes per
+//   store instruction); the combine kernel reads that layout.
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.
@@ -63,13 +69,24 @@ constexpr int kDr = 64;
 constexpr int kDkv = kDc + kDr;
 constexpr int kTile = kFastTile;                  // 32 tokens
 constexpr int kBlocks = kFastHeadsPerGroup / 16;  // 16-head blocks per group (4)
-constexpr int kThreads = 2 * 64 * kBlocks;        // one score + one accumulate wave per block
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAccWaves = 4;
+constexpr int kAccFeatureBlocks = kDc / 16 / kAccWaves;  // 16-feature blocks per accumulate wave
 constexpr int kStages = 4;                        // LDS ring depth
 constexpr int kLatBytes = kTile * kDc * 2;        // 32 KB: 32 rows of 1 KB
 constexpr int kRopeBytes = kTile * kDr * 2;       // 4 KB: 32 rows of 128 B
 constexpr int kStageBytes = kLatBytes + kRopeBytes;
+// Tile DMAs per wave: every wave copies 4 latent rows; score waves also copy
+// one block of 8 RoPE rows.
+constexpr int kLatRowsPerWave = kTile / kWaves;   // 4
+constexpr int kScoreDmas = kLatRowsPerWave + 1;   // 5
+constexpr int kAccDmas = kLatRowsPerWave;         // 4
+// LDS operand reads kept in flight, in pairs (lgkmcnt counts at most 15)
+constexpr int kScoreReadsAhead = 6;
+constexpr int kAccReadsAhead = 6;
 
-static_assert(kThreads == 512 && kTile == 32, "load mapping assumes 4 blocks and 32-token tiles");
+static_assert(kBlocks == 4 && kTile == 32, "load mapping assumes 4 head blocks and 32-token tiles");
 // Largest factor (as a power of two) by which a weight may exceed 1 before
 // the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
 constexpr float kRescaleSlack = 8.0f;
@@ -85,20 +102,22 @@ struct SplitArgs {
   const uint16_t* rope_pool;    // [P][page][64]
   const int32_t* page_table;    // [B][max_pages]
   const int32_t* context_lens;  // [B]
-  uint16_t* part_o;             // [R][S][h][512] bf16
+  uint16_t* part_o;             // [R][S][h/16][32][64][4] bf16 (register order)
   float* part_lse;              // [R][S][h]
   int batch, n_q, h, head_groups, splits, chunk_len;
   int page_size, max_pages, num_pages, max_len;
   float scale_log2;
 };
 
-// Swizzle of the 16-byte chunk index within latent row r of a tile (only
-// r mod 16 matters).  Chosen so that the score operand reads (16 rows, one
-// chunk) and the transposing reads (8 rows, two chunks) both hit distinct
-// banks with 32 or with 64 LDS banks.
+// Swizzle (an XOR on the 16-byte chunk index) of latent row r of a tile;
+// only r mod 16 matters.  A linear map of the row bits, chosen so that both
+// read patterns below are free of LDS bank conflicts on gfx950, as measured
+// with the SQ_LDS_BANK_CONFLICT counter: the score operand reads (16 rows,
+// one chunk each, 16 bytes per lane) and the transposing reads (8 rows, two
+// adjacent chunks, 8 bytes per lane).  Row bits 0, 1, 2 go to chunk bits
+// 3, 2, 1 and row bit 3 flips chunk bits 0 and 1.
 __device__ __forceinline__ int lat_swz(int r) {
-  const int k = (r >> 2) & 1;
-  return (k ^ ((r >> 3) & 1)) | ((r & 3) << 1) | (k << 3);
+  return (((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1)) ^ (((r >> 3) & 1) * 3);
 }
 // Same for the 8 chunks of a 128-byte RoPE row.
 __device__ __forceinline__ int rope_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
@@ -140,8 +159,9 @@ __device__ __forceinline__ float sum_over_token_lanes(float v) {
 }
 
 // Work-group barrier that orders LDS accesses (this wave's LDS stores have
-// completed) but leaves outstanding global->LDS DMAs alone: those are waited
-// for explicitly with vmcnt, so the next tiles stay in flight across it.
+// completed) but leaves outstanding global->LDS DMAs and global stores
+// alone: DMAs are waited for explicitly with vmcnt, so the next tiles stay
+// in flight across it.
 __device__ __forceinline__ void block_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -171,95 +191,92 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   const int b = unit / p.splits, split = unit % p.splits;
   const int m = k / p.head_groups, hgi = k % p.head_groups;
   const int r = b * p.n_q + m;
-
-  int L = p.context_lens[b];
-  L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
-  int vis = L - p.n_q + m + 1;  // query m sees tokens 0 .. L - n_q + m
-  vis = vis < 0 ? 0 : vis;
   const int t0 = split * p.chunk_len;
-  const int t1 = min(t0 + p.chunk_len, vis);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
-  const bool scorer = wave < kBlocks;
-  const int hb = wave & (kBlocks - 1);  // 16-head block of this wave
-  const int head = hgi * kFastHeadsPerGroup + 16 * hb + l16;
+  const bool scorer = wave < kWaves - kAccWaves;
 
-  uint16_t* po = p.part_o + (((size_t)r * p.splits + split) * p.h + head) * kDc;
-  float* pl = p.part_lse + ((size_t)r * p.splits + split) * p.h + head;
-
-  if (t0 >= t1) {  // nothing visible in this chunk for this query row
-    if (scorer) {
-      if (g == 0) *pl = -INFINITY;
-    } else {
-#pragma unroll 4
-      for (int fb = 0; fb < kDc / 16; ++fb) *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) = make_uint2(0, 0);
-    }
-    return;
-  }
-  const int ntiles = (t1 - t0 + kTile - 1) / kTile;  // <= kMaxFastChunkTiles (host-checked)
-  const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)sh.ring);
-
-  // Tile i -> stage i % kStages.  Score wave w copies latent rows 8w..8w+7
-  // (one 1 KB row per DMA) and RoPE rows 8w..8w+7 (one DMA); row0 is the
-  // pool row of the tile's first token.  Rows past the end of the chunk
-  // repeat the tile's first row, so the LDS never holds non-finite garbage;
-  // their probabilities are exactly 0.  Exactly 9 DMAs per score wave per
-  // tile; all address arithmetic is scalar except the lane offsets below.
-  uint32_t lat_voff[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(8 * hb + j));
-  const int rope_row = 8 * hb + (lane >> 3);
-  const uint32_t rope_chunk = 16u * (uint32_t)((lane & 7) ^ rope_swz(rope_row));
-  const uint32_t rope_voff = (uint32_t)rope_row * (kDr * 2) + rope_chunk;
-  auto issue = [&](int i, int row0) {
-    const int ts = t0 + i * kTile;
-    const int nvalid = min(kTile, t1 - ts);
-    const uint32_t sb = ring_base + (uint32_t)((i % kStages) * kStageBytes);
-    const uint8_t* lat_tile = reinterpret_cast<const uint8_t*>(p.latent_pool) + (size_t)row0 * (kDc * 2);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int rr = 8 * hb + j;
-      lds_dma16(lat_tile + (rr < nvalid ? rr : 0) * (kDc * 2), lat_voff[j], sb + rr * (kDc * 2));
-    }
-    const uint8_t* rope_tile = reinterpret_cast<const uint8_t*>(p.rope_pool) + (size_t)row0 * (kDr * 2);
-    const uint32_t voff = nvalid == kTile ? rope_voff : (rope_row < nvalid ? rope_voff : rope_chunk);
-    lds_dma16(rope_tile, voff, sb + kLatBytes + 8 * hb * (kDr * 2));
-  };
-  auto tile_pool_row = [&](int i) {
-    const int ts = t0 + i * kTile;
-    int pg = p.page_table[(size_t)b * p.max_pages + ts / p.page_size];
+  // Pool row of the tile starting at token ts of sequence b (tiles past the
+  // table clamp to its last entry; they are never used).
+  const int32_t* pt_row = p.page_table + (size_t)b * p.max_pages;
+  auto tile_pool_row = [&](int ts) {
+    int j = ts / p.page_size;
+    j = j < p.max_pages ? j : p.max_pages - 1;
+    int pg = pt_row[j];
     pg = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
     return pg * p.page_size + ts % p.page_size;
   };
-
+  // Pool rows of tiles 2.. of the chunk into LDS (every tile that can hold a
+  // visible token; all threads share the work, before the first barrier).
   auto fill_tile_rows = [&]() {
-    for (int i = 2 + tid; i < ntiles; i += kThreads) sh.tile_row[i] = tile_pool_row(i);
+    const int bound = min(p.chunk_len, max(p.max_len - t0, 0));
+    const int ntiles_max = (bound + kTile - 1) / kTile;
+    for (int i = 2 + tid; i < ntiles_max; i += kThreads) sh.tile_row[i] = tile_pool_row(t0 + i * kTile);
+  };
+  // Last visible token + 1 of this chunk for query m (tokens 0 .. L - n_q + m).
+  auto chunk_end = [&](int L) {
+    L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
+    const int vis = max(L - p.n_q + m + 1, 0);
+    return min(t0 + p.chunk_len, vis);
+  };
+  float* pl = p.part_lse + ((size_t)r * p.splits + split) * p.h + hgi * kFastHeadsPerGroup;
+
+  // Tile i -> stage i % kStages.  Wave w copies latent rows 4w..4w+3 of
+  // each tile (one 1 KB row per DMA) and, for w < 4, RoPE rows 8w..8w+7 (one
+  // DMA); row0 is the pool row of the tile's first token.  Rows past the end
+  // of the chunk repeat the tile's first row, so the LDS never holds
+  // non-finite garbage; their probabilities are exactly 0.  All address
+  // arithmetic is scalar except the lane offsets.
+  const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)sh.ring);
+  const int rope_row = 8 * (wave & 3) + (lane >> 3);
+  const uint32_t rope_chunk = 16u * (uint32_t)((lane & 7) ^ rope_swz(rope_row));
+  const uint32_t rope_voff = (uint32_t)rope_row * (kDr * 2) + rope_chunk;
+  // DMA number `part` of this wave for tile i (parts 0-3: latent rows,
+  // part 4: the RoPE block); t1 ends the chunk.
+  auto dma = [&](int i, int row0, int t1, int part, const uint32_t* lat_voff) {
+    const int nvalid = min(kTile, t1 - (t0 + i * kTile));
+    const uint32_t sb = ring_base + (uint32_t)((i % kStages) * kStageBytes);
+    if (part < kLatRowsPerWave) {
+      const int rr = kLatRowsPerWave * wave + part;
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.latent_pool) +
+                           ((size_t)row0 + (rr < nvalid ? rr : 0)) * (kDc * 2);
+      lds_dma16(src, lat_voff[part], sb + rr * (kDc * 2));
+    } else {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.rope_pool) + (size_t)row0 * (kDr * 2);
+      const uint32_t voff = rope_row < nvalid ? rope_voff : rope_chunk;
+      lds_dma16(src, voff, sb + kLatBytes + 8 * (wave & 3) * (kDr * 2));
+    }
   };
 
-  // Per-lane LDS byte offsets of the two read patterns within a stage:
-  //  score reads: row l16 (+16 tb), chunk 4s + g -> (4s) ^ c1_x with
-  //               c1_x = g ^ lat_swz(l16) < 16, i.e. base[s & 3] + 256 (s >> 2)
-  //  transposing reads: row 4g + e (+16 tb), chunk 2 fb + (q >> 1), half q & 1
-  //               -> base[fb & 7] + 256 (fb >> 3)
-  // Each role keeps all of its state inside its own branch, so that nothing
-  // of one role is live across the other's loop.
   // Iteration it (0..ntiles): score waves handle tile it, accumulate waves
-  // tile it - 1; both roles pass the same ntiles + 1 barriers.  P(k) and the
-  // rescale flags of tile k live in slot k & 1: written by the score waves
-  // between barriers k and k + 1, read by the accumulate waves between
-  // barriers k + 1 and k + 2, and overwritten (tile k + 2) only after that.
+  // tile it - 1; both roles pass the same ntiles + 2 barriers after the
+  // prologue's.  P(k) and the rescale flags of tile k live in slot k & 1:
+  // written by the score waves between barriers k and k + 1, read by the
+  // accumulate waves between barriers k + 1 and k + 2, and overwritten
+  // (tile k + 2) only after that.  The accumulate waves issue tile it + 2
+  // right after barrier it, into the stage that tile it - 2 (finished before
+  // that barrier) occupied, and wait for their share of tile it + 1 before
+  // barrier it + 1.  Each role keeps all of its state inside its own branch,
+  // so that nothing of one role is live across the other's loop.
+  uint32_t lat_voff[kLatRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kLatRowsPerWave; ++j)
+    lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(kLatRowsPerWave * wave + j));
+
   if (scorer) {
-    // ---- prologue: the first two tiles' lookups and DMAs go out first, then
-    //      the query loads, then the lookups of the remaining tiles ----
+    // ---- prologue: the length, the first tiles' and the other tiles' pool
+    //      rows and the absorbed query go out together ----
+    const int L = p.context_lens[b];
+    const int row_a = tile_pool_row(t0);
+    const int row_b = tile_pool_row(t0 + kTile);
+    fill_tile_rows();
+    const int blk = wave;  // head block within the group
+    const int head = hgi * kFastHeadsPerGroup + 16 * blk + l16;
     bf16x8 qa[kDc / 32], qr[kDr / 32];
     {
-      const int row_a = tile_pool_row(0);
-      const int row_b = ntiles > 1 ? tile_pool_row(1) : 0;
-      issue(0, row_a);
-      if (ntiles > 1) issue(1, row_b);
       const uint16_t* qa_row = p.q_abs + ((size_t)r * p.h + head) * kDc;
       const uint16_t* qr_row = p.q_r + ((size_t)r * p.h + head) * kDr;
 #pragma unroll
@@ -269,10 +286,20 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       for (int s = 0; s < kDr / 32; ++s)
         qr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr_row + 32 * s + 8 * g));
     }
-    fill_tile_rows();
-    // Consume the query registers here: waiting for them also drains the
-    // prologue DMAs (older in the same counter), after which the ring's
-    // vmcnt bookkeeping owns the counter.
+    const int t1 = chunk_end(L);
+    if (t0 >= t1) {  // nothing visible: lse = -inf, the chunk result is never read
+      if (g == 0) pl[16 * blk + l16] = -INFINITY;
+      return;
+    }
+    const int ntiles = (t1 - t0 + kTile - 1) / kTile;
+#pragma unroll
+    for (int part = 0; part < kScoreDmas; ++part) dma(0, row_a, t1, part, lat_voff);
+    if (ntiles > 1) {
+#pragma unroll
+      for (int part = 0; part < kScoreDmas; ++part) dma(1, row_b, t1, part, lat_voff);
+    }
+    // Consume the query registers here, so that the compiler's own waits for
+    // them stay out of the loop (this also waits for the first tiles).
 #pragma unroll
     for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
 #pragma unroll
@@ -280,6 +307,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // tile_row is visible, the first tiles are in LDS
 
+    // score reads: row l16 (+16 tb), chunk 4s + g -> (4s) ^ c1_x with
+    // c1_x = g ^ lat_swz(l16) < 16, i.e. base[s & 3] + 256 (s >> 2)
     const int c1_x = g ^ lat_swz(l16);
     const int rope_x = g ^ rope_swz(l16);
     uint32_t c1_base[4], rope_base[2];
@@ -289,156 +318,218 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     for (int k2 = 0; k2 < 2; ++k2) rope_base[k2] = kLatBytes + l16 * (kDr * 2) + 16 * ((4 * k2) ^ rope_x);
 
     float m_run = -INFINITY, l_run = 0.f;  // reference maximum, per-lane partial weight sum
-    for (int it = 0; it <= ntiles; ++it) {
-      if (it < ntiles) {
-        // tile `it` has landed once only the next tile's 9 DMAs are pending
-        if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+    for (int it = 0; it < ntiles; ++it) {
+      // this wave's DMAs of tile it have landed once only tile it + 1's are
+      // outstanding
+      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      static_assert(kScoreDmas == 5, "the vmcnt above counts one tile of a score wave's DMAs");
       block_barrier();
-      if (it >= ntiles) continue;
-        const int ts = t0 + it * kTile;
-        if (it + 2 < ntiles) issue(it + 2, sh.tile_row[it + 2]);
-        const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (it % kStages) * kStageBytes;
+      const bool more = it + 2 < ntiles;  // tile it + 2 goes out during this tile
+      const int row_next = more ? __builtin_amdgcn_readfirstlane(sh.tile_row[it + 2]) : 0;
+      const int ts = t0 + it * kTile;
+      const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (it % kStages) * kStageBytes;
 
-        // ---- scores: S^T[tb*16 + 4g + j][head], operands three steps ahead ----
-        auto score_operand = [&](int s, int tb) -> bf16x8 {
-          const AS3 uint8_t* src = s < kDc / 32
-              ? stage + c1_base[s & 3] + 256 * (s >> 2) + tb * 16 * (kDc * 2)
-              : stage + rope_base[s - kDc / 32] + tb * 16 * (kDr * 2);
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(src));
-        };
-        constexpr int kAhead = 3;
-        constexpr int kSteps = kDkv / 32;
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        bf16x8 opq[kAhead + 1][2];
+      // ---- scores: S^T[tb*16 + 4g + j][head], operands kAhead steps ahead ----
+      auto score_operand = [&](int s, int tb) -> bf16x8 {
+        const AS3 uint8_t* src = s < kDc / 32
+            ? stage + c1_base[s & 3] + 256 * (s >> 2) + tb * 16 * (kDc * 2)
+            : stage + rope_base[s - kDc / 32] + tb * 16 * (kDr * 2);
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(src));
+      };
+      constexpr int kAhead = kScoreReadsAhead;
+      constexpr int kSteps = kDkv / 32;
+      f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      bf16x8 opq[kAhead + 1][2];
 #pragma unroll
-        for (int s = 0; s < kAhead; ++s) {
-          opq[s][0] = score_operand(s, 0);
-          opq[s][1] = score_operand(s, 1);
-        }
+      for (int s = 0; s < kAhead; ++s) {
+        opq[s][0] = score_operand(s, 0);
+        opq[s][1] = score_operand(s, 1);
+      }
+      // The scheduling fences keep each read kAhead steps ahead of its use
+      // (the scheduler would otherwise sink reads next to their MFMAs and
+      // expose the full LDS latency on every step).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          if (s + kAhead < kSteps) {
-            opq[(s + kAhead) % (kAhead + 1)][0] = score_operand(s + kAhead, 0);
-            opq[(s + kAhead) % (kAhead + 1)][1] = score_operand(s + kAhead, 1);
-          }
-          const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
-          sacc[0] = mfma16x16x32(opq[s % (kAhead + 1)][0], bq, sacc[0]);
-          sacc[1] = mfma16x16x32(opq[s % (kAhead + 1)][1], bq, sacc[1]);
+      for (int s = 0; s < kSteps; ++s) {
+        if (s + kAhead < kSteps) {
+          opq[(s + kAhead) % (kAhead + 1)][0] = score_operand(s + kAhead, 0);
+          opq[(s + kAhead) % (kAhead + 1)][1] = score_operand(s + kAhead, 1);
         }
+        const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
+        sacc[0] = mfma16x16x32(opq[s % (kAhead + 1)][0], bq, sacc[0]);
+        sacc[1] = mfma16x16x32(opq[s % (kAhead + 1)][1], bq, sacc[1]);
+        if ((s & 3) == 1 && more) dma(it + 2, row_next, t1, s >> 2, lat_voff);  // s = 1, 5, 9, 13, 17
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
-        // ---- online softmax (base 2), per lane = per head ----
-        // m_run is a reference maximum, not necessarily the exact running
-        // max: it moves only when a score exceeds it by more than
-        // kRescaleSlack, so weights stay below 2^kRescaleSlack and most tiles
-        // need no rescale.  The final division by l makes the result
-        // independent of the reference.  Scores stay unscaled until the
-        // exponent (scale > 0, so maxima commute with it).
-        if (ts + kTile > t1) {  // the chunk's last tile: tokens past t1 weigh 0
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              if (ts + tb * 16 + 4 * g + j >= t1) sacc[tb][j] = -INFINITY;
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                           fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-        tmax = max_over_token_lanes(tmax) * p.scale_log2;
-        const int slot = it & 1;
-        if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
-          const float m_new = fmaxf(m_run, tmax);
-          // nothing has been accumulated before the first tile: no rescale
-          const int flag = m_run != -INFINITY;
-          if (flag) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-            if (g == 0) sh.alpha[slot][16 * hb + l16] = alpha;
-          }
-          if (lane == 0) sh.rescale[slot][hb] = flag;
-          m_run = m_new;
-        } else if (lane == 0) {
-          sh.rescale[slot][hb] = 0;
-        }
-        f32x8 pf;
+      // ---- online softmax (base 2), per lane = per head ----
+      // m_run is a reference maximum, not necessarily the exact running
+      // max: it moves only when a score exceeds it by more than
+      // kRescaleSlack, so weights stay below 2^kRescaleSlack and most tiles
+      // need no rescale.  The final division by l makes the result
+      // independent of the reference.  Scores stay unscaled until the
+      // exponent (scale > 0, so maxima commute with it).
+      const int slot = it & 1;
+      if (ts + kTile > t1) {  // the chunk's last tile: tokens past t1 weigh 0
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            pf[tb * 4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][j], p.scale_log2, -m_run));
-        const bf16x8 pb = __builtin_convertvector(pf, bf16x8);  // round to nearest even
-        sh.prob[slot][hb][lane] = __builtin_bit_cast(u32x4, pb);
-        // sum of the weights the MFMA sees (bf16), two per dot2
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 two = {pb[e], pb[e + 1]};
-          psum = __builtin_amdgcn_fdot2_f32_bf16(two, one, psum, false);
+            if (ts + tb * 16 + 4 * g + j >= t1) sacc[tb][j] = -INFINITY;
+      }
+      float tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+      tmax = max_over_token_lanes(tmax) * p.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m_run, tmax);
+        // nothing has been accumulated before the first tile: no rescale
+        const int flag = m_run != -INFINITY;
+        if (flag) {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+          if (g == 0) sh.alpha[slot][16 * blk + l16] = alpha;
         }
-        l_run += psum;
+        if (lane == 0) sh.rescale[slot][blk] = flag;
+        m_run = m_new;
+      } else if (lane == 0) {
+        sh.rescale[slot][blk] = 0;
+      }
+      f32x8 pf;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pf[tb * 4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][j], p.scale_log2, -m_run));
+      const bf16x8 pb = __builtin_convertvector(pf, bf16x8);  // round to nearest even
+      sh.prob[slot][blk][lane] = __builtin_bit_cast(u32x4, pb);
+      // sum of the weights the MFMA sees (bf16), two per dot2
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 two = {pb[e], pb[e + 1]};
+        psum = __builtin_amdgcn_fdot2_f32_bf16(two, one, psum, false);
+      }
+      l_run += psum;
     }
+    block_barrier();  // iteration ntiles: the accumulate waves fold the last tile
     const float l_tot = sum_over_token_lanes(l_run);
     if (g == 0) {
-      *pl = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-      sh.inv_l[16 * hb + l16] = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      pl[16 * blk + l16] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+      sh.inv_l[16 * blk + l16] = l_tot > 0.f ? 1.f / l_tot : 0.f;
     }
-  } else {
-    fill_tile_rows();
-    __syncthreads();  // pairs with the score waves' prologue barrier
-
-    const int tr_row = 4 * g + (l16 >> 2);
-    const int tr_x = ((l16 & 3) >> 1) ^ lat_swz(tr_row);
-    uint32_t tr_base[8];
-#pragma unroll
-    for (int k2 = 0; k2 < 8; ++k2)
-      tr_base[k2] = tr_row * (kDc * 2) + 16 * ((2 * k2) ^ tr_x) + 8 * (l16 & 1);
-
-    f32x4 acc[kDc / 16];
-#pragma unroll
-    for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int it = 0; it <= ntiles; ++it) {
-      block_barrier();
-      if (it == 0) continue;
-      const int j = it - 1;  // tile folded in this iteration
-      const int slot = j & 1;
-      if (sh.rescale[slot][hb] != 0) {  // the reference maximum moved
-        const float alpha = sh.alpha[slot][16 * hb + l16];
-#pragma unroll
-        for (int fb = 0; fb < kDc / 16; ++fb) acc[fb] *= alpha;
-      }
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, sh.prob[slot][hb][lane]);
-      const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (j % kStages) * kStageBytes;
-
-      // ---- latent accumulation: O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
-      auto latent_operand = [&](int fb) -> bf16x8 {
-        const AS3 uint8_t* a0 = stage + tr_base[fb & 7] + 256 * (fb >> 3);
-        const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)a0));
-        const u16x4 hi = __builtin_bit_cast(
-            u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)(a0 + 16 * (kDc * 2))));
-        const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        return as_bf16x8(v);
-      };
-      bf16x8 cur = latent_operand(0);
-#pragma unroll
-      for (int fb = 0; fb < kDc / 16; ++fb) {
-        bf16x8 nxt = cur;
-        if (fb + 1 < kDc / 16) nxt = latent_operand(fb + 1);
-        acc[fb] = mfma16x16x32(cur, pb, acc[fb]);
-        cur = nxt;
-      }
-    }
-    __syncthreads();  // inv_l is visible
-    const float inv = sh.inv_l[16 * hb + l16];
-#pragma unroll
-    for (int fb = 0; fb < kDc / 16; ++fb) {
-      const f32x4 v = acc[fb] * inv;
-      *reinterpret_cast<uint2*>(po + fb * 16 + 4 * g) =
-          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    }
+    block_barrier();  // inv_l is visible
     return;
   }
-  __syncthreads();  // pairs with the accumulate waves' barrier above
+
+  // ---- accumulate waves: issue the tile DMAs; fold features
+  //      [128 a, 128 a + 128) of all 64 heads ----
+  const int a = wave - (kWaves - kAccWaves);
+  // prologue: the length and the first two tiles' pool rows (scalar loads)
+  // go out together with the other tiles' pool rows
+  const int L = p.context_lens[b];
+  const int row_a = tile_pool_row(t0);
+  const int row_b = tile_pool_row(t0 + kTile);
+  fill_tile_rows();
+  const int t1 = chunk_end(L);
+  if (t0 >= t1) return;  // the score waves write lse = -inf
+  const int ntiles = (t1 - t0 + kTile - 1) / kTile;  // <= kMaxFastChunkTiles (host-checked)
+
+#pragma unroll
+  for (int part = 0; part < kAccDmas; ++part) dma(0, row_a, t1, part, lat_voff);
+  if (ntiles > 1) {
+#pragma unroll
+    for (int part = 0; part < kAccDmas; ++part) dma(1, row_b, t1, part, lat_voff);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // tile_row is visible, the first tiles are in LDS
+
+  // transposing reads: row 4g + e (+16 for the upper 16 tokens), chunk
+  // 2 fb + (q >> 1), half q & 1 -> base[fb & 7] + 256 (fb >> 3)
+  const int tr_row = 4 * g + (l16 >> 2);
+  const int tr_x = ((l16 & 3) >> 1) ^ lat_swz(tr_row);
+  uint32_t tr_base[8];
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) tr_base[k2] = tr_row * (kDc * 2) + 16 * ((2 * k2) ^ tr_x) + 8 * (l16 & 1);
+
+  f32x4 acc[kAccFeatureBlocks][kBlocks];
+#pragma unroll
+  for (int fb = 0; fb < kAccFeatureBlocks; ++fb)
+#pragma unroll
+    for (int hb = 0; hb < kBlocks; ++hb) acc[fb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int it = 0; it <= ntiles; ++it) {
+    if (it < ntiles) {  // this wave's DMAs of tile it have landed
+      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      static_assert(kAccDmas == 4, "the vmcnt above counts one tile of an accumulate wave's DMAs");
+    }
+    block_barrier();
+    const bool more = it + 2 < ntiles;  // tile it + 2 goes out during this iteration
+    const int row_next = more ? __builtin_amdgcn_readfirstlane(sh.tile_row[it + 2]) : 0;
+    if (it == 0) {
+      if (more) {
+#pragma unroll
+        for (int part = 0; part < kAccDmas; ++part) dma(2, row_next, t1, part, lat_voff);
+      }
+      continue;
+    }
+    const int j = it - 1;  // tile folded in this iteration
+    const int slot = j & 1;
+#pragma unroll
+    for (int hb = 0; hb < kBlocks; ++hb) {
+      if (sh.rescale[slot][hb] != 0) {  // the reference maximum moved (rare)
+        const float alpha = sh.alpha[slot][16 * hb + l16];
+#pragma unroll
+        for (int fb = 0; fb < kAccFeatureBlocks; ++fb) acc[fb][hb] *= alpha;
+      }
+    }
+    bf16x8 pb[kBlocks];
+#pragma unroll
+    for (int hb = 0; hb < kBlocks; ++hb) pb[hb] = __builtin_bit_cast(bf16x8, sh.prob[slot][hb][lane]);
+    const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (j % kStages) * kStageBytes;
+
+    // ---- O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
+    auto latent_operand = [&](int fbl) -> bf16x8 {
+      const int fb = kAccFeatureBlocks * a + fbl;  // feature block of the tile
+      const AS3 uint8_t* a0 = stage + tr_base[fb & 7] + 256 * (fb >> 3);
+      const u16x4 lo = __builtin_bit_cast(u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)a0));
+      const u16x4 hi = __builtin_bit_cast(
+          u16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((AS3 tr_vec*)(a0 + 16 * (kDc * 2))));
+      const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return as_bf16x8(v);
+    };
+    constexpr int kAhead = kAccReadsAhead;
+    bf16x8 opq[kAhead + 1];
+#pragma unroll
+    for (int fb = 0; fb < kAhead; ++fb) opq[fb] = latent_operand(fb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (as for the scores)
+#pragma unroll
+    for (int fb = 0; fb < kAccFeatureBlocks; ++fb) {
+      if (fb + kAhead < kAccFeatureBlocks) opq[(fb + kAhead) % (kAhead + 1)] = latent_operand(fb + kAhead);
+#pragma unroll
+      for (int hb = 0; hb < kBlocks; ++hb)
+        acc[fb][hb] = mfma16x16x32(opq[fb % (kAhead + 1)], pb[hb], acc[fb][hb]);
+      if ((fb & 1) == 0 && more) dma(it + 2, row_next, t1, fb >> 1, lat_voff);  // fb = 0, 2, 4, 6
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  block_barrier();  // pairs with the score waves' barrier after their lse
+  // chunk result in register order: [r][split][h/16][32][64][4]
+  uint16_t* po = p.part_o + ((size_t)r * p.splits + split) * p.h * kDc;
+#pragma unroll
+  for (int hb = 0; hb < kBlocks; ++hb) {
+    const float inv = sh.inv_l[16 * hb + l16];
+    const int hblk = hgi * kBlocks + hb;
+#pragma unroll
+    for (int fbl = 0; fbl < kAccFeatureBlocks; ++fbl) {
+      const int fb = kAccFeatureBlocks * a + fbl;
+      const f32x4 v = acc[fbl][hb] * inv;
+      *reinterpret_cast<uint2*>(po + (((size_t)hblk * (kDc / 16) + fb) * 64 + lane) * 4) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+    }
+  }
 }
 
 }  // namespace

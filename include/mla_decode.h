@@ -137,8 +137,10 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
 mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs);
 
 /* Waits for the recorded events, writes the summed milliseconds of each of
- * the four kernels over the recorded runs into ms[0..3] and the number of
- * runs into *runs, then starts a new recording. */
+ * the four steps over the recorded runs into ms[0..3] and the number of runs
+ * into *runs, then starts a new recording.  On the bf16 fast path the chunk
+ * merge and the up-projection run as one kernel, reported in ms[2]; ms[3]
+ * is then 0. */
 mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs);
 
 /* Releases a plan.  NULL is accepted and ignored. */

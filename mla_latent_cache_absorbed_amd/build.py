@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"
 
-SOURCES = ["decode.cpp", "q_absorb.hip", "split_attn.hip", "combine.hip", "up_project.hip",
+SOURCES = ["decode.cpp", "q_absorb.hip", "split_attn.hip", "finish.hip", "combine.hip",
            "general.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

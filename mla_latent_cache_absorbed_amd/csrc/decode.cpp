@@ -50,7 +50,7 @@ mla_status_t fail(mla_status_t st, const char* fmt, ...) {
 // A chunk is never shorter than this many tokens unless the context is:
 // each chunk writes h * d_c * 4 bytes of partial result, which must stay
 // small next to the chunk's own cache bytes ((d_c + d_r) * 2 per token).
-constexpr int kMinChunkTokens = 256;
+constexpr int kMinChunkTokens = 128;
 // Work-groups per CU the split kernel is sized for.
 constexpr int kGroupsPerCu = 1;
 
@@ -118,7 +118,8 @@ Layout layout_for(const mla_decode_plan& p, int batch, int n_q, int splits) {
   l.part_o = l.q_abs + align256(R * h * d_c * inter);
   l.part_lse = l.part_o + align256(R * splits * h * d_c * inter);
   l.c_bar = l.part_lse + align256(R * splits * h * 4);
-  l.total = l.c_bar + align256(R * h * d_c * inter);
+  // the fast path merges the chunks straight into the up-projection
+  l.total = l.c_bar + (p.fast ? 0 : align256(R * h * d_c * inter));
   return l;
 }
 
@@ -283,8 +284,11 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
     switch (k) {
       case 0: e = p.fast ? mla::launch_q_absorb_bf16(a, c) : mla::launch_q_absorb_general(a, c); break;
       case 1: e = p.fast ? mla::launch_split_attn_bf16(a, c) : mla::launch_split_attn_general(a, c); break;
-      case 2: e = mla::launch_combine(a, p.fast, c); break;
-      default: e = p.fast ? mla::launch_up_project_bf16(a, c) : mla::launch_up_project_general(a, c); break;
+      case 2: e = p.fast ? mla::launch_finish_bf16(a, c) : mla::launch_combine_general(a, c); break;
+      default:
+        if (p.fast) continue;  // folded into the finish kernel
+        e = mla::launch_up_project_general(a, c);
+        break;
     }
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
@@ -322,12 +326,15 @@ mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs)
   for (int k = 0; k < kKernels; ++k) ms[k] = 0.f;
   const int n = plan->timing_runs;
   if (n > 0) {
-    hipError_t st = hipEventSynchronize(plan->events[(size_t)n * kEventsPerRun - 1]);
+    // the stop event of the last kernel the plan launches
+    const int last = plan->fast ? 2 : 3;
+    hipError_t st = hipEventSynchronize(plan->events[(size_t)(n - 1) * kEventsPerRun + 2 * last + 1]);
     if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(st));
   }
   for (int r = 0; r < n; ++r) {
     const hipEvent_t* ev = &plan->events[(size_t)r * kEventsPerRun];
     for (int k = 0; k < kKernels; ++k) {
+      if (plan->fast && k == 3) continue;  // no separate up-projection kernel
       float t = 0.f;
       hipError_t st = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
       if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(st));

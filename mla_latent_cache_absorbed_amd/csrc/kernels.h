@@ -31,11 +31,10 @@ struct DecodeArgs {
 
   // workspace carve-up
   void* q_abs;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
-  void* part_o;     // chunk results, already normalised.  Fast path: bf16 in
-                    // the split kernel's register order [R][S][h/16][32][64][4]
-                    // (see combine.hip); general path: f32 [R][S][h][d_c]
+  void* part_o;     // [R][S][h][d_c]   chunk results already normalised: bf16
+                    //                  (fast path) or f32 (general path)
   float* part_lse;  // [R][S][h]        f32, base-2 log-sum-exp of each chunk
-  void* c_bar;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
+  void* c_bar;      // [R][h][d_c]      f32 (general path only)
 };
 
 // Where a kernel is launched.  With both events set, the launch records
@@ -67,15 +66,15 @@ constexpr int kMaxFastChunkTiles = 1024;
 // page_size % 32 == 0.
 hipError_t launch_q_absorb_bf16(const DecodeArgs& a, const LaunchCtx& s);
 hipError_t launch_split_attn_bf16(const DecodeArgs& a, const LaunchCtx& s);
-hipError_t launch_up_project_bf16(const DecodeArgs& a, const LaunchCtx& s);
+// Chunk merge and W_UV up-projection in one kernel.
+hipError_t launch_finish_bf16(const DecodeArgs& a, const LaunchCtx& s);
 
 // General path: any dims (d_c <= 1024), f32 or bf16 storage, f32 math.
 hipError_t launch_q_absorb_general(const DecodeArgs& a, const LaunchCtx& s);
 hipError_t launch_split_attn_general(const DecodeArgs& a, const LaunchCtx& s);
 hipError_t launch_up_project_general(const DecodeArgs& a, const LaunchCtx& s);
 
-// Log-sum-exp merge of the chunk results into c_bar: bf16 partials and
-// c_bar on the fast path, f32 on the general path.
-hipError_t launch_combine(const DecodeArgs& a, bool fast, const LaunchCtx& s);
+// Log-sum-exp merge of the f32 chunk results into c_bar (general path).
+hipError_t launch_combine_general(const DecodeArgs& a, const LaunchCtx& s);
 
 }  // namespace mla

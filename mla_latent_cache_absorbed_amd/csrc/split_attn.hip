@@ -52,8 +52,8 @@
 //   for e = 0..3).  P comes out of the score accumulators already in the
 //   matching B-operand order, so it crosses LDS as one 16-byte store and load
 //   per lane and head block.
-// - The chunk result is stored in register order (512 contiguous bytes per
-//   store instruction); the combine kernel reads that layout.
+// - The chunk result is transposed to head-major order through the (by then
+//   free) LDS ring, so that every wave stores whole 1 KB head rows.
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.
@@ -94,6 +94,7 @@ constexpr float kRescaleSlack = 8.0f;
 #define AS3 __attribute__((address_space(3)))
 typedef short tr_vec __attribute__((vector_size(8)));  // operand type of the transposing read
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct SplitArgs {
   const uint16_t* q_abs;        // [R][h][512]
@@ -102,7 +103,7 @@ struct SplitArgs {
   const uint16_t* rope_pool;    // [P][page][64]
   const int32_t* page_table;    // [B][max_pages]
   const int32_t* context_lens;  // [B]
-  uint16_t* part_o;             // [R][S][h/16][32][64][4] bf16 (register order)
+  uint16_t* part_o;             // [R][S][h][512] bf16
   float* part_lse;              // [R][S][h]
   int batch, n_q, h, head_groups, splits, chunk_len;
   int page_size, max_pages, num_pages, max_len;
@@ -168,6 +169,13 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Chunk result, head-major in the (then free) tile ring: head row of 1 KB,
+// its 32-byte granules XOR-swizzled by the head so that the accumulate
+// waves' 8-byte writes (16 heads x 32 bytes each) spread over the banks.
+__device__ __forceinline__ uint32_t result_offset(int head, int feature) {
+  return (uint32_t)head * (kDc * 2) + 32u * (uint32_t)((feature >> 4) ^ (head & 15)) + 2u * (feature & 15);
+}
+
 struct Shared {
   uint8_t ring[kStages * kStageBytes];  // the tile ring (token-major, swizzled)
   u32x4 prob[2][kBlocks][64];           // P(k) per 16-head block, in B-operand order
@@ -223,6 +231,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     return min(t0 + p.chunk_len, vis);
   };
   float* pl = p.part_lse + ((size_t)r * p.splits + split) * p.h + hgi * kFastHeadsPerGroup;
+
+  // The chunk result leaves LDS one 1 KB head row per wave instruction:
+  // [R][S][h][d_c] bf16, each wave storing 8 of the 64 heads.
+  auto store_result = [&]() {
+    uint16_t* po = p.part_o + (((size_t)r * p.splits + split) * p.h + hgi * kFastHeadsPerGroup) * kDc;
+#pragma unroll
+    for (int k2 = 0; k2 < kFastHeadsPerGroup / kWaves; ++k2) {
+      const int head = (kFastHeadsPerGroup / kWaves) * wave + k2;
+      const u32x4 v = *reinterpret_cast<const AS3 u32x4*>((AS3 uint8_t*)sh.ring + result_offset(head, 8 * lane));
+      *reinterpret_cast<u32x4*>(po + (size_t)head * kDc + 8 * lane) = v;
+    }
+  };
 
   // Tile i -> stage i % kStages.  Wave w copies latent rows 4w..4w+3 of
   // each tile (one 1 KB row per DMA) and, for w < 4, RoPE rows 8w..8w+7 (one
@@ -420,6 +440,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       sh.inv_l[16 * blk + l16] = l_tot > 0.f ? 1.f / l_tot : 0.f;
     }
     block_barrier();  // inv_l is visible
+    block_barrier();  // the accumulate waves have written the result into LDS
+    store_result();
     return;
   }
 
@@ -516,20 +538,21 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     }
   }
   block_barrier();  // pairs with the score waves' barrier after their lse
-  // chunk result in register order: [r][split][h/16][32][64][4]
-  uint16_t* po = p.part_o + ((size_t)r * p.splits + split) * p.h * kDc;
+  // normalised result (bf16) into LDS, head-major, then out by all waves
 #pragma unroll
   for (int hb = 0; hb < kBlocks; ++hb) {
     const float inv = sh.inv_l[16 * hb + l16];
-    const int hblk = hgi * kBlocks + hb;
+    const int head = 16 * hb + l16;
 #pragma unroll
     for (int fbl = 0; fbl < kAccFeatureBlocks; ++fbl) {
-      const int fb = kAccFeatureBlocks * a + fbl;
+      const int f0 = 16 * (kAccFeatureBlocks * a + fbl) + 4 * g;  // D[4g + j][l16]
       const f32x4 v = acc[fbl][hb] * inv;
-      *reinterpret_cast<uint2*>(po + (((size_t)hblk * (kDc / 16) + fb) * 64 + lane) * 4) =
-          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      *reinterpret_cast<AS3 u32x2*>((AS3 uint8_t*)sh.ring + result_offset(head, f0)) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }
+  block_barrier();
+  store_result();
 }
 
 }  // namespace

@@ -31,8 +31,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNELS = {
     "q_absorb": ("q_absorb", "q_absorb.hip"),
     "split_attn": ("split_attn", "split_attn.hip"),
-    "combine": ("combine", "combine.hip"),
-    "up_project": ("up_project", "up_project.hip"),
+    "finish": ("finish", "finish.hip"),
+    "combine": ("combine_general", "combine.hip"),
+    "up_project": ("up_general", "general.hip"),
 }
 
 

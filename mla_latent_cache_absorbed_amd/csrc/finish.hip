@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
       const size_t stride = (size_t)h * kDc;  // elements per chunk
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       float wsum = 0.f;
-      constexpr int kUnroll = 4;
+      constexpr int kUnroll = 16;  // chunks in flight per lane
       for (int s0 = wave; s0 < splits; s0 += kGroups * kUnroll) {
         float l[kUnroll];
         uint4 v[kUnroll];

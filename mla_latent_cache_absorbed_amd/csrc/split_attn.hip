@@ -21,9 +21,10 @@
 //       16x16x32 bf16 MFMA, the online softmax, and the bf16 probabilities
 //       P(k) published to LDS (plus per-head rescale factors when the
 //       reference moves);
-//     accumulate waves 4-7 (128 latent features each, all 64 heads): fold
-//       P(k-1) into the fp32 latent accumulator against tile k-1; every
-//       latent operand they read feeds four MFMAs, one per head block.
+//     accumulate waves 4-7 (128 latent features each, all 64 heads): issue
+//       the tile DMAs and fold P(k-1) into the fp32 latent accumulator
+//       against tile k-1; every latent operand they read feeds four MFMAs,
+//       one per head block.
 //   Each SIMD runs one wave of each role, so one role's LDS latency is
 //   covered by the other's MFMAs, and each role fits in 256 registers.  One
 //   work-group barrier per tile orders everything.
@@ -31,8 +32,9 @@
 //   filled by direct global->LDS DMA (global_load_lds_dwordx4): no staging
 //   registers; tiles k+1 and k+2 are in flight while the score waves read
 //   tile k and the accumulate waves tile k-1.  A DMA instruction holds its
-//   wave at issue for a while, so all eight waves share the 36 DMAs of a
-//   tile and issue them between their MFMAs.  A tile never straddles a
+//   wave at issue for a while, so the accumulate waves issue them while the
+//   score waves' MFMAs run, and run their own MFMAs while the score waves
+//   do the softmax arithmetic.  A tile never straddles a
 //   cache page (pages are multiples of 32 tokens), so each tile is one
 //   contiguous run of 32 latent rows and 32 RoPE rows in the pool; every
 //   tile's pool row is looked up once at the start, in parallel with the
@@ -77,11 +79,9 @@ constexpr int kStages = 4;                        // LDS ring depth
 constexpr int kLatBytes = kTile * kDc * 2;        // 32 KB: 32 rows of 1 KB
 constexpr int kRopeBytes = kTile * kDr * 2;       // 4 KB: 32 rows of 128 B
 constexpr int kStageBytes = kLatBytes + kRopeBytes;
-// Tile DMAs per wave: every wave copies 4 latent rows; score waves also copy
-// one block of 8 RoPE rows.
-constexpr int kLatRowsPerWave = kTile / kWaves;   // 4
-constexpr int kScoreDmas = kLatRowsPerWave + 1;   // 5
-constexpr int kAccDmas = kLatRowsPerWave;         // 4
+// Tile DMAs per accumulate wave: 8 latent rows and one block of 8 RoPE rows.
+constexpr int kLatRowsPerWave = kTile / kAccWaves;  // 8
+constexpr int kAccDmas = kLatRowsPerWave + 1;       // 9
 // LDS operand reads kept in flight, in pairs (lgkmcnt counts at most 15)
 constexpr int kScoreReadsAhead = 6;
 constexpr int kAccReadsAhead = 6;
@@ -180,7 +180,7 @@ struct Shared {
   uint8_t ring[kStages * kStageBytes];  // the tile ring (token-major, swizzled)
   u32x4 prob[2][kBlocks][64];           // P(k) per 16-head block, in B-operand order
   float alpha[2][kBlocks * 16];         // rescale factor per head when flagged
-  int rescale[2][kBlocks];              // per block: accumulator must be rescaled
+  u32x4 rescale[2];                     // per 16-head block: accumulator must be rescaled
   float inv_l[kBlocks * 16];            // 1 / sum of weights, per head, at the end
   int tile_row[kMaxFastChunkTiles];     // pool row of each tile's first token
 };
@@ -244,30 +244,31 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     }
   };
 
-  // Tile i -> stage i % kStages.  Wave w copies latent rows 4w..4w+3 of
-  // each tile (one 1 KB row per DMA) and, for w < 4, RoPE rows 8w..8w+7 (one
+  // Tile i -> stage i % kStages.  Accumulate wave a copies latent rows
+  // 8a..8a+7 of each tile (one 1 KB row per DMA) and RoPE rows 8a..8a+7 (one
   // DMA); row0 is the pool row of the tile's first token.  Rows past the end
   // of the chunk repeat the tile's first row, so the LDS never holds
   // non-finite garbage; their probabilities are exactly 0.  All address
   // arithmetic is scalar except the lane offsets.
   const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)sh.ring);
-  const int rope_row = 8 * (wave & 3) + (lane >> 3);
+  const int dma_wave = wave & 3;  // accumulate wave index
+  const int rope_row = 8 * dma_wave + (lane >> 3);
   const uint32_t rope_chunk = 16u * (uint32_t)((lane & 7) ^ rope_swz(rope_row));
   const uint32_t rope_voff = (uint32_t)rope_row * (kDr * 2) + rope_chunk;
-  // DMA number `part` of this wave for tile i (parts 0-3: latent rows,
-  // part 4: the RoPE block); t1 ends the chunk.
+  // DMA number `part` of this wave for tile i (parts 0-7: latent rows,
+  // part 8: the RoPE block); t1 ends the chunk.
   auto dma = [&](int i, int row0, int t1, int part, const uint32_t* lat_voff) {
     const int nvalid = min(kTile, t1 - (t0 + i * kTile));
     const uint32_t sb = ring_base + (uint32_t)((i % kStages) * kStageBytes);
     if (part < kLatRowsPerWave) {
-      const int rr = kLatRowsPerWave * wave + part;
+      const int rr = kLatRowsPerWave * dma_wave + part;
       const uint8_t* src = reinterpret_cast<const uint8_t*>(p.latent_pool) +
                            ((size_t)row0 + (rr < nvalid ? rr : 0)) * (kDc * 2);
       lds_dma16(src, lat_voff[part], sb + rr * (kDc * 2));
     } else {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(p.rope_pool) + (size_t)row0 * (kDr * 2);
       const uint32_t voff = rope_row < nvalid ? rope_voff : rope_chunk;
-      lds_dma16(src, voff, sb + kLatBytes + 8 * (wave & 3) * (kDr * 2));
+      lds_dma16(src, voff, sb + kLatBytes + 8 * dma_wave * (kDr * 2));
     }
   };
 
@@ -281,17 +282,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   // that barrier) occupied, and wait for their share of tile it + 1 before
   // barrier it + 1.  Each role keeps all of its state inside its own branch,
   // so that nothing of one role is live across the other's loop.
-  uint32_t lat_voff[kLatRowsPerWave];
-#pragma unroll
-  for (int j = 0; j < kLatRowsPerWave; ++j)
-    lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(kLatRowsPerWave * wave + j));
-
   if (scorer) {
     // ---- prologue: the length, the first tiles' and the other tiles' pool
     //      rows and the absorbed query go out together ----
     const int L = p.context_lens[b];
-    const int row_a = tile_pool_row(t0);
-    const int row_b = tile_pool_row(t0 + kTile);
     fill_tile_rows();
     const int blk = wave;  // head block within the group
     const int head = hgi * kFastHeadsPerGroup + 16 * blk + l16;
@@ -312,14 +306,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       return;
     }
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-#pragma unroll
-    for (int part = 0; part < kScoreDmas; ++part) dma(0, row_a, t1, part, lat_voff);
-    if (ntiles > 1) {
-#pragma unroll
-      for (int part = 0; part < kScoreDmas; ++part) dma(1, row_b, t1, part, lat_voff);
-    }
     // Consume the query registers here, so that the compiler's own waits for
-    // them stay out of the loop (this also waits for the first tiles).
+    // them stay out of the loop.
 #pragma unroll
     for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
 #pragma unroll
@@ -339,14 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
 
     float m_run = -INFINITY, l_run = 0.f;  // reference maximum, per-lane partial weight sum
     for (int it = 0; it < ntiles; ++it) {
-      // this wave's DMAs of tile it have landed once only tile it + 1's are
-      // outstanding
-      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      static_assert(kScoreDmas == 5, "the vmcnt above counts one tile of a score wave's DMAs");
       block_barrier();
-      const bool more = it + 2 < ntiles;  // tile it + 2 goes out during this tile
-      const int row_next = more ? __builtin_amdgcn_readfirstlane(sh.tile_row[it + 2]) : 0;
       const int ts = t0 + it * kTile;
       const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (it % kStages) * kStageBytes;
 
@@ -379,7 +360,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
         const bf16x8 bq = s < kDc / 32 ? qa[s] : qr[s - kDc / 32];
         sacc[0] = mfma16x16x32(opq[s % (kAhead + 1)][0], bq, sacc[0]);
         sacc[1] = mfma16x16x32(opq[s % (kAhead + 1)][1], bq, sacc[1]);
-        if ((s & 3) == 1 && more) dma(it + 2, row_next, t1, s >> 2, lat_voff);  // s = 1, 5, 9, 13, 17
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -454,6 +434,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   const int row_a = tile_pool_row(t0);
   const int row_b = tile_pool_row(t0 + kTile);
   fill_tile_rows();
+  uint32_t lat_voff[kLatRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kLatRowsPerWave; ++j)
+    lat_voff[j] = 16u * (uint32_t)(lane ^ lat_swz(kLatRowsPerWave * a + j));
   const int t1 = chunk_end(L);
   if (t0 >= t1) return;  // the score waves write lse = -inf
   const int ntiles = (t1 - t0 + kTile - 1) / kTile;  // <= kMaxFastChunkTiles (host-checked)
@@ -483,9 +467,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
 
   for (int it = 0; it <= ntiles; ++it) {
     if (it < ntiles) {  // this wave's DMAs of tile it have landed
-      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      static_assert(kAccDmas == 4, "the vmcnt above counts one tile of an accumulate wave's DMAs");
+      static_assert(kAccDmas == 9, "the vmcnt above counts one tile of an accumulate wave's DMAs");
     }
     block_barrier();
     const bool more = it + 2 < ntiles;  // tile it + 2 goes out during this iteration
@@ -499,20 +483,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     }
     const int j = it - 1;  // tile folded in this iteration
     const int slot = j & 1;
-#pragma unroll
-    for (int hb = 0; hb < kBlocks; ++hb) {
-      if (sh.rescale[slot][hb] != 0) {  // the reference maximum moved (rare)
-        const float alpha = sh.alpha[slot][16 * hb + l16];
-#pragma unroll
-        for (int fb = 0; fb < kAccFeatureBlocks; ++fb) acc[fb][hb] *= alpha;
-      }
-    }
-    bf16x8 pb[kBlocks];
-#pragma unroll
-    for (int hb = 0; hb < kBlocks; ++hb) pb[hb] = __builtin_bit_cast(bf16x8, sh.prob[slot][hb][lane]);
     const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (j % kStages) * kStageBytes;
-
-    // ---- O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
     auto latent_operand = [&](int fbl) -> bf16x8 {
       const int fb = kAccFeatureBlocks * a + fbl;  // feature block of the tile
       const AS3 uint8_t* a0 = stage + tr_base[fb & 7] + 256 * (fb >> 3);
@@ -522,18 +493,40 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       const u16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       return as_bf16x8(v);
     };
+    // The four rescale flags, P(j) and the first latent operands go out
+    // together; the tile DMAs are issued while they land (a DMA holds the
+    // wave at issue), and the MFMAs follow.
+    const u32x4 flags = sh.rescale[slot];
+    bf16x8 pb[kBlocks];
+#pragma unroll
+    for (int hb = 0; hb < kBlocks; ++hb) pb[hb] = __builtin_bit_cast(bf16x8, sh.prob[slot][hb][lane]);
     constexpr int kAhead = kAccReadsAhead;
     bf16x8 opq[kAhead + 1];
 #pragma unroll
     for (int fb = 0; fb < kAhead; ++fb) opq[fb] = latent_operand(fb);
+    if (more) {
+#pragma unroll
+      for (int part = 0; part < kAccDmas; ++part) dma(it + 2, row_next, t1, part, lat_voff);
+    }
+    if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {  // the reference maximum moved (rare)
+#pragma unroll
+      for (int hb = 0; hb < kBlocks; ++hb) {
+        if (flags[hb] != 0) {
+          const float alpha = sh.alpha[slot][16 * hb + l16];
+#pragma unroll
+          for (int fb = 0; fb < kAccFeatureBlocks; ++fb) acc[fb][hb] *= alpha;
+        }
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead (as for the scores)
+
+    // ---- O^T[f][head] += C^T[f][tokens] . P^T[tokens][head] ----
 #pragma unroll
     for (int fb = 0; fb < kAccFeatureBlocks; ++fb) {
       if (fb + kAhead < kAccFeatureBlocks) opq[(fb + kAhead) % (kAhead + 1)] = latent_operand(fb + kAhead);
 #pragma unroll
       for (int hb = 0; hb < kBlocks; ++hb)
         acc[fb][hb] = mfma16x16x32(opq[fb % (kAhead + 1)], pb[hb], acc[fb][hb]);
-      if ((fb & 1) == 0 && more) dma(it + 2, row_next, t1, fb >> 1, lat_voff);  // fb = 0, 2, 4, 6
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -3,7 +3,8 @@
 // For query row r and head i the split kernel left one normalised latent
 // o_s (bf16, [R][S][h][512]) and one base-2 log-sum-exp lse_s (fp32) per
 // context chunk s.  This kernel forms
-//   c_bar = sum_s w_s o_s / sum_s w_s,   w_s = 2^(lse_s - max_s lse_s)
+//   c_bar = sum_s w_s o_s / sum_s w_s,   w_s = 2^(lse_s - m)
+// for any reference m (here running maxima, merged at the end)
 // (the softmax over the whole visible context evaluated chunk by chunk: the
 // chunks partition the token axis, so the merge is exact up to rounding;
 // "MLA, dim by dim" section 5.2) and then
@@ -52,6 +53,32 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
   const int g = lane >> 4, l16 = lane & 15;
   const int a_base = 64 * blockIdx.y + 16 * wave;  // this wave's 16 output rows
 
+  constexpr int kUnroll = 16;              // chunks in flight per lane
+  const size_t stride = (size_t)h * kDc;   // elements of one chunk's results
+  // One batch of the merge: the lse and the 8 features of this lane of the
+  // chunks s0, s0 + 4, ... of row r (chunks past the end read as empty).
+  auto load_batch = [&](int r, int s0, float* l, uint4* v) {
+    const float* lse = part_lse + (size_t)r * splits * h + head;
+    const uint16_t* src = part_o + ((size_t)r * splits * h + head) * kDc + 8 * lane;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int s = s0 + kGroups * u;
+      if (s < splits) {  // uniform per wave
+        l[u] = lse[(size_t)s * h];
+        v[u] = *reinterpret_cast<const uint4*>(src + s * stride);
+      } else {
+        l[u] = -INFINITY;
+        v[u] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  // The first batch goes out before the weight rows: loads complete in
+  // order, so the merge then need not wait for the weight stream.
+  float l_first[kUnroll];
+  uint4 v_first[kUnroll];
+  if (rows <= 0) return;  // (the host launches no empty batch)
+  load_batch(0, wave, l_first, v_first);
+
   // W_UV[head] rows a_base .. a_base + 15 as the A operand: lane (g, l16)
   // holds row l16, d_c elements 32 s + 8 g .. + 7 for step s.
   const uint16_t* wrow = w_uv + ((size_t)head * kDh + a_base + l16) * kDc;
@@ -65,34 +92,31 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
     // ---- combine: c_bar of rows rb .. rb + nr - 1 into LDS ----
     for (int rr = 0; rr < nr; ++rr) {
       const int r = rb + rr;
-      const float* lse = part_lse + (size_t)r * splits * h + head;
-      float mx = -INFINITY;
-      for (int s = tid; s < splits; s += kThreads) mx = fmaxf(mx, lse[(size_t)s * h]);
-#pragma unroll
-      for (int mask = 32; mask >= 1; mask >>= 1) mx = xor_max(mx, mask);
-      if (lane == 0) red[wave] = mx;
-      __syncthreads();
-      mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-      // lane covers features 8 lane .. 8 lane + 7; group `wave` every 4th chunk
-      const uint16_t* src = part_o + ((size_t)r * splits * h + head) * kDc + 8 * lane;
-      const size_t stride = (size_t)h * kDc;  // elements per chunk
+      // lane covers features 8 lane .. 8 lane + 7; wave `wave` takes every
+      // 4th chunk with its own running maximum, the four are merged below
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      float wsum = 0.f;
-      constexpr int kUnroll = 16;  // chunks in flight per lane
+      float wsum = 0.f, mx = -INFINITY;
       for (int s0 = wave; s0 < splits; s0 += kGroups * kUnroll) {
         float l[kUnroll];
         uint4 v[kUnroll];
+        if (r == 0 && s0 == wave) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {  // all loads first, several chunks in flight
-          const int s = s0 + kGroups * u;
-          if (s < splits) {  // uniform per wave
-            l[u] = lse[(size_t)s * h];
-            v[u] = *reinterpret_cast<const uint4*>(src + s * stride);
-          } else {
-            l[u] = -INFINITY;
-            v[u] = make_uint4(0, 0, 0, 0);
+          for (int u = 0; u < kUnroll; ++u) {
+            l[u] = l_first[u];
+            v[u] = v_first[u];
           }
+        } else {
+          load_batch(r, s0, l, v);
+        }
+        float bmx = l[0];  // the same in every lane (one head)
+#pragma unroll
+        for (int u = 1; u < kUnroll; ++u) bmx = fmaxf(bmx, l[u]);
+        if (bmx > mx) {  // raise the reference of what is summed so far
+          const float f = mx == -INFINITY ? 0.f : exp2f(mx - bmx);
+          acc0 *= f;
+          acc1 *= f;
+          wsum *= f;
+          mx = bmx;
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -120,14 +144,24 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
         part_acc[wave - 1][lane][0] = acc0;
         part_acc[wave - 1][lane][1] = acc1;
         part_w[wave - 1][lane] = wsum;
+        if (lane == 0) red[wave] = mx;
       }
       __syncthreads();
       if (wave == 0) {
+        float mall = mx;
+#pragma unroll
+        for (int k = 1; k < kGroups; ++k) mall = fmaxf(mall, red[k]);
+        const float f0 = mx == -INFINITY ? 0.f : exp2f(mx - mall);
+        acc0 *= f0;
+        acc1 *= f0;
+        wsum *= f0;
 #pragma unroll
         for (int k = 0; k < kGroups - 1; ++k) {
-          acc0 += part_acc[k][lane][0];
-          acc1 += part_acc[k][lane][1];
-          wsum += part_w[k][lane];
+          const float mk = red[k + 1];
+          const float fk = mk == -INFINITY ? 0.f : exp2f(mk - mall);
+          acc0 += fk * part_acc[k][lane][0];
+          acc1 += fk * part_acc[k][lane][1];
+          wsum += fk * part_w[k][lane];
         }
         const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
         acc0 *= inv;

@@ -49,15 +49,15 @@ def counts(wl, splits):
     proj_flops = 2 * R * wl.h * wl.d_h * wl.d_c
     w_bytes = wl.h * wl.d_h * wl.d_c * el
     cache_bytes = wl.cache_tokens() * (wl.d_c + wl.d_r) * el
-    part_bytes = R * splits * wl.h * (wl.d_c + 1) * 4
+    # chunk partials: bf16 latent + fp32 lse on the bf16 fast path, fp32 otherwise
+    part_bytes = R * splits * wl.h * (wl.d_c * el + 4)
     return {
         "q_absorb": dict(bytes=w_bytes + R * wl.h * (wl.d_h * el + wl.d_c * 2), flops=proj_flops),
         "split_attn": dict(bytes=cache_bytes, flops=pairs * per_pair, partial_bytes=part_bytes),
         "combine": dict(bytes=part_bytes + R * wl.h * wl.d_c * 2, flops=0),
         "up_project": dict(bytes=w_bytes + R * wl.h * (wl.d_c * 2 + wl.d_h * el), flops=proj_flops),
         # chunk merge fused with the up-projection (bf16 fast path)
-        "finish": dict(bytes=R * splits * wl.h * (wl.d_c * 2 + 4) + w_bytes + R * wl.h * wl.d_h * el,
-                       flops=proj_flops),
+        "finish": dict(bytes=part_bytes + w_bytes + R * wl.h * wl.d_h * el, flops=proj_flops),
         "step": dict(bytes=cache_bytes + 2 * w_bytes, flops=pairs * per_pair + 2 * proj_flops,
                      cache_bytes=cache_bytes),
     }
@@ -144,6 +144,43 @@ def time_steps(dw, layers, steps, warmup, per_kernel):
     return step_s, kernels
 
 
+def achievable_peaks():
+    """What plain library work reaches on this GPU, for context beside the
+    vendor peaks: a 1 GiB device-to-device copy (read + write bytes) and a
+    bf16 8192^3 GEMM (hipBLASLt through torch), each timed with events."""
+    import torch
+    res = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    res["copy_gbps"] = 2 * n * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    m = 8192
+    a = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(m, m, device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    res["gemm_bf16_tflops"] = 2 * m ** 3 * reps / (e0.elapsed_time(e1) / 1e3) / 1e12
+    res["what"] = ("1 GiB device-to-device copy (torch copy_, read + write bytes) and a bf16 "
+                   "8192x8192x8192 torch.mm, 10 timed repetitions each")
+    return res
+
+
 def cpu_baseline(wl, target_s=15.0):
     """Time the fp64 oracle (explicit K/V form, as it stands) on a bounded
     sample of the workload: whole decode of a subset of (sequence, head)
@@ -193,8 +230,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ds2_t4k")
-    ap.add_argument("--extra", default="ds2_t32k",
-                    help="second workload whose split kernel is also measured ('' = none)")
+    ap.add_argument("--extra", default="ds2_t32k,ds2_t128k,ds2_paged_b32,ds2_mtp_b16",
+                    help="comma-separated further workloads whose steps and split kernel are "
+                         "also measured ('' = none)")
+    ap.add_argument("--no-achievable", action="store_true",
+                    help="skip the copy and GEMM measurements of achievable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="0 = enough for 1 GiB")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -272,15 +312,29 @@ def main():
         "kernels": {k: dict(avg_us=kern[k] * 1e6, **rooflines[k]) for k in kern},
     }
 
-    if args.extra:
-        wl2, dw2, c2, step2, kern2, s2, ch2, nl2 = measure(args.extra, max(10, args.steps // 2), 5)
-        out["split_kernel_" + wl2.name] = dict(
-            avg_us=kern2["split_attn"] * 1e6, splits=s2, chunk_len=ch2,
-            cache_gbps=c2["split_attn"]["bytes"] / kern2["split_attn"] / 1e9,
-            tflops=c2["split_attn"]["flops"] / kern2["split_attn"] / 1e12,
-            step_us=step2 * 1e6, kernels_us={k: v * 1e6 for k, v in kern2.items()},
-            roofline=kernel_roofline("split_attn", c2["split_attn"], kern2["split_attn"], wl2.dtype))
+    sweep = {}
+    for name in [n for n in args.extra.split(",") if n]:
+        wl2, dw2, c2, step2, kern2, s2, ch2, nl2 = measure(name, max(10, args.steps // 2), 5)
+        t_split = kern2["split_attn"]
+        sweep[wl2.name] = dict(
+            split_us=t_split * 1e6, splits=s2, chunk_len=ch2, layers_rotated=nl2,
+            cache_gbps=c2["split_attn"]["bytes"] / t_split / 1e9,
+            cache_plus_partials_gbps=(c2["split_attn"]["bytes"] + c2["split_attn"]["partial_bytes"])
+            / t_split / 1e9,
+            tflops=c2["split_attn"]["flops"] / t_split / 1e12,
+            step_us=step2 * 1e6, step_tflops=c2["step"]["flops"] / step2 / 1e12,
+            kernels_us={k: v * 1e6 for k, v in kern2.items()},
+            roofline=kernel_roofline("split_attn", c2["split_attn"], t_split, wl2.dtype))
+        log("%s: step %.2f us; kernels (us): %s" % (name, step2 * 1e6,
+                                                   {k: round(v * 1e6, 2) for k, v in kern2.items()}))
         del dw2
+    if sweep:
+        out["sweep"] = sweep
+        if "ds2_t32k" in sweep:  # the point the split kernel's roofline bar is set at
+            out["split_kernel_ds2_t32k"] = dict(sweep["ds2_t32k"])
+
+    if not args.no_achievable:
+        out["achievable"] = achievable_peaks()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

@@ -171,6 +171,19 @@ def test_ragged_lengths_and_tails(torch, splits):
           "ragged lengths S=%d" % splits)
 
 
+@pytest.mark.parametrize("splits", [5, 12, 20])
+def test_chunk_merge_over_row_blocks(torch, splits):
+    """20 query rows (a full and a partial block of 16 in the merge) with
+    chunk counts that select each merge variant; the short sequences leave
+    trailing chunks empty."""
+    lens = [1, 2, 40, 64, 65, 100, 127, 128, 129, 200, 255, 256, 300, 333, 400, 480, 511, 512,
+            600, 639]
+    wl = inputs.make("ds2_t4k", batch=len(lens), lens=("list", lens), shuffled=True, seed=205)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16",
+          "merge over row blocks S=%d" % splits)
+
+
 def test_single_token_context_returns_projected_latent(torch):
     wl = inputs.make("ds2_t4k", lens=("fixed", 1), seed=202)
     dw = _run(wl, torch, out_dtype="f32")

@@ -51,8 +51,9 @@ def counts(wl, splits):
     cache_bytes = wl.cache_tokens() * (wl.d_c + wl.d_r) * el
     # chunk partials: bf16 latent + fp32 lse on the bf16 fast path, fp32 otherwise
     part_bytes = R * splits * wl.h * (wl.d_c * el + 4)
+    absorb_bytes = w_bytes + R * wl.h * (wl.d_h * el + wl.d_c * 2)
     return {
-        "q_absorb": dict(bytes=w_bytes + R * wl.h * (wl.d_h * el + wl.d_c * 2), flops=proj_flops),
+        "q_absorb": dict(bytes=absorb_bytes, flops=proj_flops),
         "split_attn": dict(bytes=cache_bytes, flops=pairs * per_pair, partial_bytes=part_bytes),
         "combine": dict(bytes=part_bytes + R * wl.h * wl.d_c * 2, flops=0),
         "up_project": dict(bytes=w_bytes + R * wl.h * (wl.d_c * 2 + wl.d_h * el), flops=proj_flops),
@@ -181,6 +182,38 @@ def achievable_peaks():
     return res
 
 
+def time_graph(dw, layers, steps, warmup):
+    """Average step time (s) of the same steps replayed from one HIP graph
+    that holds one step per layer set (the launches of mla_decode_run are
+    captured from torch's current stream)."""
+    import torch
+    n = len(layers)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(n):
+            dw.run(**layers.sets[i])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            dw.run(**layers.sets[i])
+    for _ in range(max(1, warmup // n)):
+        graph.replay()
+    reps = max(1, math.ceil(steps / n))
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    del graph
+    return start.elapsed_time(end) / 1e3 / (reps * n)
+
+
 def cpu_baseline(wl, target_s=15.0):
     """Time the fp64 oracle (explicit K/V form, as it stands) on a bounded
     sample of the workload: whole decode of a subset of (sequence, head)
@@ -273,12 +306,15 @@ def main():
         log("%s: %d layers rotated (%.0f MB each), %d chunks of %d tokens" %
             (name, n_layers, layer_bytes(wl) / 1e6, splits, chunk))
         step_s, _ = time_steps(dw, layers, steps, warmup, per_kernel=False)
+        graph_s = time_graph(dw, layers, steps, warmup)
+        log("%s: step %.2f us eager, %.2f us replayed from a HIP graph" % (name, step_s * 1e6, graph_s * 1e6))
         _, kern = time_steps(dw, layers, steps, 2, per_kernel=True)
         c = counts(wl, splits)
         del layers
-        return wl, dw, c, step_s, kern, splits, chunk, n_layers
+        return wl, dw, c, step_s, graph_s, kern, splits, chunk, n_layers
 
-    wl, dw, c, step_s, kern, splits, chunk, n_layers = measure(args.workload, args.steps, args.warmup)
+    wl, dw, c, step_s, graph_s, kern, splits, chunk, n_layers = measure(args.workload, args.steps,
+                                                                       args.warmup)
     log("step %.2f us; kernels (us): %s" % (step_s * 1e6, {k: round(v * 1e6, 2) for k, v in kern.items()}))
 
     rooflines = {k: kernel_roofline(k, c[k], kern[k], wl.dtype) for k in kern}
@@ -298,6 +334,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_s * 1e3,
+        "graph_ms_per_step": graph_s * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -312,19 +349,25 @@ def main():
         "kernels": {k: dict(avg_us=kern[k] * 1e6, **rooflines[k]) for k in kern},
     }
 
+    def split_entry(wl2, c2, kern2, s2, ch2, nl2, step2=None, graph2=None):
+        k = "split_attn"
+        t_split = kern2[k]
+        e = dict(split_us=t_split * 1e6, splits=s2, chunk_len=ch2, layers_rotated=nl2,
+                 cache_gbps=c2["split_attn"]["bytes"] / t_split / 1e9,
+                 cache_plus_partials_gbps=(c2["split_attn"]["bytes"] + c2["split_attn"]["partial_bytes"])
+                 / t_split / 1e9,
+                 tflops=c2["split_attn"]["flops"] / t_split / 1e12,
+                 kernels_us={kk: v * 1e6 for kk, v in kern2.items()},
+                 roofline=kernel_roofline(k, c2[k], t_split, wl2.dtype))
+        if step2 is not None:
+            e.update(step_us=step2 * 1e6, step_tflops=c2["step"]["flops"] / step2 / 1e12,
+                     graph_step_us=graph2 * 1e6)
+        return e
+
     sweep = {}
     for name in [n for n in args.extra.split(",") if n]:
-        wl2, dw2, c2, step2, kern2, s2, ch2, nl2 = measure(name, max(10, args.steps // 2), 5)
-        t_split = kern2["split_attn"]
-        sweep[wl2.name] = dict(
-            split_us=t_split * 1e6, splits=s2, chunk_len=ch2, layers_rotated=nl2,
-            cache_gbps=c2["split_attn"]["bytes"] / t_split / 1e9,
-            cache_plus_partials_gbps=(c2["split_attn"]["bytes"] + c2["split_attn"]["partial_bytes"])
-            / t_split / 1e9,
-            tflops=c2["split_attn"]["flops"] / t_split / 1e12,
-            step_us=step2 * 1e6, step_tflops=c2["step"]["flops"] / step2 / 1e12,
-            kernels_us={k: v * 1e6 for k, v in kern2.items()},
-            roofline=kernel_roofline("split_attn", c2["split_attn"], t_split, wl2.dtype))
+        wl2, dw2, c2, step2, graph2, kern2, s2, ch2, nl2 = measure(name, max(10, args.steps // 2), 5)
+        sweep[wl2.name] = split_entry(wl2, c2, kern2, s2, ch2, nl2, step2, graph2)
         log("%s: step %.2f us; kernels (us): %s" % (name, step2 * 1e6,
                                                    {k: round(v * 1e6, 2) for k, v in kern2.items()}))
         del dw2

@@ -52,6 +52,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// LDS (address space 3) pointers, and the operand type of the transposing
+// LDS read ds_read_b64_tr_b16.
+#define AS3 __attribute__((address_space(3)))
+typedef short tr_vec __attribute__((vector_size(8)));
+
+// One wave-wide DMA of 64 x 16 bytes from global memory into LDS
+// (global_load_lds_dwordx4): lane l reads sbase + voff[l] (a uniform 64-bit
+// base in SGPRs plus a per-lane 32-bit offset) and writes lds_base + 16 l.
+// Issued by hand so that the compiler does not serialise DMA rings with
+// conservative waits; callers track completion with explicit vmcnt waits.
+// No output registers are involved; M0 (the LDS base of the DMA) is saved
+// and restored around it.
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
 // Wave-wide reductions over lanes that differ in the given xor bit(s).
 __device__ __forceinline__ float xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));

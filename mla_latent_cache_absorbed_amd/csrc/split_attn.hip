@@ -91,8 +91,6 @@ static_assert(kBlocks == 4 && kTile == 32, "load mapping assumes 4 head blocks a
 // the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
 constexpr float kRescaleSlack = 8.0f;
 
-#define AS3 __attribute__((address_space(3)))
-typedef short tr_vec __attribute__((vector_size(8)));  // operand type of the transposing read
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -122,25 +120,6 @@ __device__ __forceinline__ int lat_swz(int r) {
 }
 // Same for the 8 chunks of a 128-byte RoPE row.
 __device__ __forceinline__ int rope_swz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
-
-// One wave-wide DMA of 64 x 16 bytes from global memory into LDS: lane l
-// reads sbase + voff[l] (a uniform 64-bit base in SGPRs plus a per-lane
-// 32-bit offset) and writes lds_base + 16 l.  Issued by hand so that the
-// compiler does not serialise the ring with conservative waits; completion
-// is tracked with explicit vmcnt waits below.  No output registers are
-// involved; M0 (the LDS base of the DMA) is saved and restored around it.
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "v"(voff), "s"(sbase)
-      : "memory");
-}
 
 // The four lanes l, l^16, l^32, l^48 hold the same head (different tokens):
 // reduce across them with the gfx950 cross-row swaps instead of LDS

@@ -38,9 +38,11 @@ KERNELS = {
 
 
 def source_digest(kernel: str) -> str:
-    """Digest of the files that determine one kernel's code."""
+    """Digest of the files that determine one kernel's code (its source and
+    every shared header)."""
     h = hashlib.sha256()
-    for f in (KERNELS[kernel][1], "common.h", "kernels.h"):
+    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
+    for f in [KERNELS[kernel][1]] + headers:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -40,8 +40,38 @@ def log(msg):
     sys.stderr.flush()
 
 
-def counts(wl, splits):
-    """Algorithmic bytes and FLOPs of one step, per kernel."""
+def chunk_count(wl, splits, chunk, num_cus):
+    """Chunks of the step: batch * splits for a fixed chunking; for one
+    planned on the device ((0, 0) from mla_decode_split_plan) the same choice
+    the kernels make from the context lengths, redone here for the byte
+    counts."""
+    if splits > 0:
+        return wl.batch * splits
+    lens = [min(max(int(L), 0), int(wl.max_len)) for L in wl.lens]
+    total = sum(lens)
+    target = max(1, num_cus // (wl.n_q * (wl.h // 64)))
+
+    def length(parts):
+        c = -(-(-(-total // max(parts, 1))) // 32) * 32
+        return min(max(c, 128), 1024 * 32)
+
+    def count(c):
+        return sum(-(-L // c) for L in lens)
+    parts = target
+    for _ in range(3):
+        c = length(parts)
+        n = count(c)
+        if n <= target or c == 1024 * 32:
+            return n
+        parts -= n - target
+        if parts < 1:
+            break
+    return count(length(target - wl.batch))
+
+
+def counts(wl, chunks):
+    """Algorithmic bytes and FLOPs of one step, per kernel (`chunks`: chunk
+    results of one query token, over all sequences)."""
     el = 2 if wl.dtype == "bf16" else 4
     R = wl.rows
     pairs = wl.visible_pairs()
@@ -50,7 +80,7 @@ def counts(wl, splits):
     w_bytes = wl.h * wl.d_h * wl.d_c * el
     cache_bytes = wl.cache_tokens() * (wl.d_c + wl.d_r) * el
     # chunk partials: bf16 latent + fp32 lse on the bf16 fast path, fp32 otherwise
-    part_bytes = R * splits * wl.h * (wl.d_c * el + 4)
+    part_bytes = chunks * wl.n_q * wl.h * (wl.d_c * el + 4)
     absorb_bytes = w_bytes + R * wl.h * (wl.d_h * el + wl.d_c * 2)
     return {
         "q_absorb": dict(bytes=absorb_bytes, flops=proj_flops),
@@ -309,7 +339,7 @@ def main():
         graph_s = time_graph(dw, layers, steps, warmup)
         log("%s: step %.2f us eager, %.2f us replayed from a HIP graph" % (name, step_s * 1e6, graph_s * 1e6))
         _, kern = time_steps(dw, layers, steps, 2, per_kernel=True)
-        c = counts(wl, splits)
+        c = counts(wl, chunk_count(wl, splits, chunk, torch.cuda.get_device_properties(0).multi_processor_count))
         del layers
         return wl, dw, c, step_s, graph_s, kern, splits, chunk, n_layers
 

@@ -100,7 +100,11 @@ size_t mla_decode_workspace_size(mla_decode_t plan, int32_t batch, int32_t n_q,
 
 /* Chunking the plan would use for this batch shape: number of chunks per
  * sequence and tokens per chunk.  Host only; lets callers and tests see the
- * split decision. */
+ * split decision.  (0, 0) means that the chunking is decided on the device
+ * from the context lengths: on the bf16 fast path with several sequences and
+ * no forced count, one chunk length is chosen for the call so that the
+ * chunks of all sequences (a long sequence gets more, a short one fewer)
+ * fill the GPU evenly. */
 mla_status_t mla_decode_split_plan(mla_decode_t plan, int32_t batch, int32_t n_q,
                                    int32_t max_context_len, int32_t* num_splits,
                                    int32_t* chunk_len);

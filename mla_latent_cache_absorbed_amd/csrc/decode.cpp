@@ -78,8 +78,16 @@ int query_num_cus() {
 }
 
 struct Split {
-  int splits, chunk_len;
+  int splits, chunk_len;  // fixed chunking: chunks per sequence, tokens per chunk
+  // fast path: chunk results are stored per global chunk; `planned`: the
+  // chunking is decided on the device from the context lengths (about
+  // `target` chunks in all), `chunks` bounds their number
+  bool planned = false;
+  int chunks = 0, target = 0;
 };
+
+// Longest chunk of a planned chunking (the fast split kernel's tile table).
+constexpr int kMaxPlannedChunk = mla::kMaxFastChunkTiles * mla::kFastTile;
 
 // Chunks per sequence: enough work-groups to fill the CUs, but chunks no
 // shorter than kMinChunkTokens; a forced count from the config wins.
@@ -101,6 +109,24 @@ Split plan_splits(const mla_decode_plan& p, int batch, int n_q, int max_len) {
   Split r;
   r.chunk_len = ceil_div(ceil_div(max_len, s), gran) * gran;
   r.splits = std::max(1, ceil_div(max_len, r.chunk_len));
+  r.chunks = batch * r.splits;
+  // Several sequences of unknown (possibly very different) lengths: one
+  // chunk length for the call, chosen on the device from the actual lengths
+  // so that every work-group gets about the same number of tiles.  Worth its
+  // extra dependent load (the lengths before the page table, and again in
+  // the merge) when a sequence gets more than two chunks on average; with
+  // fewer, the fixed chunking keeps the work-groups of equal-length
+  // sequences just as even.
+  if (p.fast && p.cfg.num_splits == 0 && batch > 1) {
+    const int target = std::max(1, kGroupsPerCu * p.num_cus / groups_per_chunk);
+    if (target > 2 * batch) {
+      r.planned = true;
+      r.target = target;
+      // the device's choice keeps the count within the target, unless the
+      // chunk length reaches its maximum (then n <= total / max + batch)
+      r.chunks = std::max(target, batch + ceil_div((long long)batch * max_len, kMaxPlannedChunk));
+    }
+  }
   return r;
 }
 
@@ -110,14 +136,16 @@ struct Layout {
   size_t q_abs, part_o, part_lse, c_bar, total;
 };
 
-Layout layout_for(const mla_decode_plan& p, int batch, int n_q, int splits) {
+Layout layout_for(const mla_decode_plan& p, int batch, int n_q, const Split& sp) {
   const size_t R = (size_t)batch * n_q, h = p.cfg.h, d_c = p.cfg.d_c;
   const size_t inter = p.fast ? 2 : 4;  // bytes per q_abs / partial / c_bar element
+  // chunk results: [chunks][n_q] rows on the fast path, [R][S] otherwise
+  const size_t parts = p.fast ? (size_t)sp.chunks * n_q : R * sp.splits;
   Layout l;
   l.q_abs = 0;
   l.part_o = l.q_abs + align256(R * h * d_c * inter);
-  l.part_lse = l.part_o + align256(R * splits * h * d_c * inter);
-  l.c_bar = l.part_lse + align256(R * splits * h * 4);
+  l.part_lse = l.part_o + align256(parts * h * d_c * inter);
+  l.c_bar = l.part_lse + align256(parts * h * 4);
   // the fast path merges the chunks straight into the up-projection
   l.total = l.c_bar + (p.fast ? 0 : align256(R * h * d_c * inter));
   return l;
@@ -186,7 +214,7 @@ size_t mla_decode_workspace_size(mla_decode_t plan, int32_t batch, int32_t n_q,
   if (check_shape(plan, batch, n_q, max_context_len) != MLA_OK) return 0;
   if (batch == 0) return 0;
   const Split s = plan_splits(*plan, batch, n_q, max_context_len);
-  return layout_for(*plan, batch, n_q, s.splits).total;
+  return layout_for(*plan, batch, n_q, s).total;
 }
 
 mla_status_t mla_decode_split_plan(mla_decode_t plan, int32_t batch, int32_t n_q,
@@ -196,8 +224,8 @@ mla_status_t mla_decode_split_plan(mla_decode_t plan, int32_t batch, int32_t n_q
   if (st != MLA_OK) return st;
   if (!num_splits || !chunk_len) return fail(MLA_ERR_INVALID_ARG, "output pointers are NULL");
   const Split s = plan_splits(*plan, batch, n_q, max_context_len);
-  *num_splits = s.splits;
-  *chunk_len = s.chunk_len;
+  *num_splits = s.planned ? 0 : s.splits;
+  *chunk_len = s.planned ? 0 : s.chunk_len;
   return MLA_OK;
 }
 
@@ -234,7 +262,7 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
     return fail(MLA_ERR_INVALID_ARG, "page_table and context_lens must be 4-byte aligned");
 
   const Split s = plan_splits(p, batch, n_q, max_context_len);
-  const Layout l = layout_for(p, batch, n_q, s.splits);
+  const Layout l = layout_for(p, batch, n_q, s);
   if (workspace_bytes < l.total)
     return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, l.total);
 
@@ -251,6 +279,11 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
   a.max_len = max_context_len;
   a.splits = s.splits;
   a.chunk_len = s.chunk_len;
+  a.planned = s.planned;
+  a.chunks = s.chunks;
+  a.plan_target = s.target;
+  a.plan_min_chunk = kMinChunkTokens;
+  a.plan_max_chunk = kMaxPlannedChunk;
   a.in_bf16 = c.dtype == MLA_DTYPE_BF16;
   a.out_bf16 = p.out_dtype == MLA_DTYPE_BF16;
   a.scale_log2 = p.scale * 1.4426950408889634f;  // exp(x) = 2^(x log2 e)

@@ -14,6 +14,12 @@
 // Transformers to Modern LLMs ... Part 3" section 3.g).  Chunks with
 // lse = -inf (nothing visible) weigh 0 and their result is never used.
 //
+// The chunk results of query row r = (sequence b, token m) are those of
+// chunks first_b .. first_b + n_b - 1, stored [chunk][n_q][h][d_c] (lse
+// [chunk][n_q][h]): with a fixed chunking first_b = S b and n_b = S; with the
+// chunking planned from the context lengths (chunk_plan.h) the same device
+// computation that placed the split kernel's work-groups gives them.
+//
 // One work-group per (head, 64 rows of W_UV[i], 16 query rows): the W_UV
 // rows stream from HBM straight into the MFMA A operand (rows of W as M, d_c
 // as K) while c_bar of the 16 query rows is built in LDS from the chunk
@@ -25,7 +31,7 @@
 //   every (row, chunk) load of a batch in flight at once;
 // - many chunks: all four waves merge one row, each with every fourth chunk
 //   and its own running maximum, and the four partial sums meet in LDS.
-#include "common.h"
+#include "chunk_plan.h"
 #include "kernels.h"
 
 namespace mla {
@@ -37,7 +43,7 @@ constexpr int kDh = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowBlock = 16;  // query rows per work-group (the MFMA N)
-constexpr int kBatch = 16;     // chunk loads in flight per lane
+constexpr int kMergeBatch = 16;  // chunk loads in flight per lane
 
 // Physical 16-byte chunk of logical chunk c in c_bar row `row` (< 16): the
 // XOR spreads the B-operand reads (16 rows, one chunk each) over the banks.
@@ -48,6 +54,38 @@ struct MergeShared {
   f32x4 part_acc[kWaves - 1][64][2];
   float part_w[kWaves - 1][64];
   float red[kWaves];
+  int row_first[kRowBlock];  // planned chunking: first chunk of each row
+  int row_count[kRowBlock];  // and its number of chunks
+  int max_count;
+};
+
+struct FinishArgs {
+  const uint16_t* part_o;
+  const float* part_lse;
+  const uint16_t* w_uv;
+  void* out;
+  const int32_t* context_lens;
+  int rows, n_q, h, batch, max_len;
+  int slots;  // > 0: fixed chunking, `slots` chunks per sequence; 0: planned
+  int plan_target, plan_min, plan_max;  // planned chunking (chunk_plan.h)
+};
+
+// Where the chunk results of the rows of one block are: lse index of chunk 0
+// of row rb + rr (this head), the index step from one chunk to the next, and
+// the row's number of chunks.
+// (The planned tables are read through LDS pointers: a generic pointer
+// would make the compiler wait for every global load in flight.)
+struct RowMap {
+  const AS3 int* first;  // planned: row_first, row_count in LDS
+  const AS3 int* count_;
+  int rb, head, n_q, h, slots;
+  __device__ __forceinline__ size_t base(int rr) const {
+    const int r = rb + rr, b = r / n_q, m = r - b * n_q;
+    const int g0 = slots > 0 ? b * slots : first[rr];
+    return ((size_t)g0 * n_q + m) * h + head;
+  }
+  __device__ __forceinline__ size_t step() const { return (size_t)n_q * h; }
+  __device__ __forceinline__ int count(int rr) const { return slots > 0 ? slots : count_[rr]; }
 };
 
 // Weighted sum of one batch of chunk results into (acc0, acc1, wsum) with
@@ -85,63 +123,65 @@ __device__ __forceinline__ u32x4 pack_row(f32x4 acc0, f32x4 acc1, float wsum) {
                pack_bf16x2(acc1[0], acc1[1]), pack_bf16x2(acc1[2], acc1[3])};
 }
 
-// kSlots > 0: each wave merges 16 / kSlots whole rows per batch, kSlots
-// chunk slots per row (kSlots >= S, a power of two).  kSlots == 0: the
-// four waves share each row's chunks.
-template <bool kBf16Out, int kSlots>
-__global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* __restrict__ part_o,
-                                                               const float* __restrict__ part_lse,
-                                                               const uint16_t* __restrict__ w_uv,
-                                                               void* __restrict__ out, int rows,
-                                                               int splits, int h) {
-  __shared__ __attribute__((aligned(16))) MergeShared sh;
+// The block's merge and up-projection.  kSlots > 0: each wave merges
+// 16 / kSlots whole rows per batch, kSlots chunk slots per row (kSlots >= any
+// row's chunk count, a power of two).  kSlots == 0: the four waves share each
+// row's chunks.
+// W_UV[head] rows a_base + 16 wave .. + 15 as the A operand: lane (g, l16)
+// holds row l16, d_c elements 32 s + 8 g .. + 7 for step s.
+__device__ __forceinline__ void load_weights(const FinishArgs& f, int head, int a_base, int wave, int lane,
+                                             bf16x8* wa) {
+  const uint16_t* wrow = f.w_uv + ((size_t)head * kDh + a_base + 16 * wave + (lane & 15)) * kDc;
+#pragma unroll
+  for (int s = 0; s < kDc / 32; ++s)
+    wa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(wrow + 32 * s + 8 * (lane >> 4)));
+  // keep the weight loads here, in flight during what follows (the
+  // scheduler would otherwise move them after the merge arithmetic)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
-  // blockIdx.x = head + h * (W_UV half + 2 * row block): congruent mod 8
-  // for one head when h % 8 == 0
-  const int head = blockIdx.x % h;
-  const int rest = blockIdx.x / h;
-  const int a_base = 64 * (rest & 1);
-  const int rb = kRowBlock * (rest >> 1);
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
+// kPreloaded: the caller has loaded the weight rows into wa already.
+// kBatch: chunk loads in flight per lane when the waves share a row.
+template <bool kBf16Out, int kSlots, bool kPreloaded = false, int kBatch = kMergeBatch>
+__device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh, const RowMap& rm, int head,
+                                            int a_base, int rb, int nr, int wave, int lane, bf16x8* wa) {
+  const int h = f.h;
   const int g = lane >> 4, l16 = lane & 15;
-  const int nr = min(kRowBlock, rows - rb);
-  if (nr <= 0) return;  // (the host launches no empty block)
-
-  const size_t stride = (size_t)h * kDc;  // elements of one chunk's results
-  // lse and this lane's 8 features of chunk s of row r (row < rows, s < splits)
-  auto lse_at = [&](int r, int s) { return part_lse[((size_t)r * splits + s) * h + head]; };
-  auto res_at = [&](int r, int s) {
-    return *reinterpret_cast<const uint4*>(part_o + ((size_t)r * splits * h + head) * kDc + s * stride +
-                                           8 * lane);
+  // lse and this lane's 8 features of chunk s of row rb + rr (s < count(rr))
+  auto lse_at = [&](int rr, int s) { return f.part_lse[rm.base(rr) + (size_t)s * rm.step()]; };
+  auto res_at = [&](int rr, int s) {
+    return *reinterpret_cast<const uint4*>(f.part_o + (rm.base(rr) + (size_t)s * rm.step()) * kDc + 8 * lane);
   };
 
   // ---- first batch of chunk loads, ahead of the weight rows (loads
   //      complete in order, so the merge need not wait for the weights) ----
-  constexpr int kRowsPerBatch = kSlots > 0 ? kBatch / kSlots : 1;
-  float l_first[kBatch];
-  uint4 v_first[kBatch];
+  // few chunks: 16 (row, chunk) loads per batch; many: kBatch chunks of a row
+  constexpr int kItems = kSlots > 0 ? kMergeBatch : kBatch;
+  constexpr int kRowsPerBatch = kSlots > 0 ? kMergeBatch / kSlots : 1;
+  float l_first[kItems];
+  uint4 v_first[kItems];
   auto load_rows = [&](int row0, float* l, uint4* v) {  // kSlots > 0: rows row0 .. + kRowsPerBatch - 1
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = 0; u < kItems; ++u) {
       const int rr = row0 + u / (kSlots > 0 ? kSlots : 1), s = u % (kSlots > 0 ? kSlots : 1);
-      if (rr < nr && s < splits) {  // uniform per wave
-        l[u] = lse_at(rb + rr, s);
-        v[u] = res_at(rb + rr, s);
+      if (rr < nr && s < rm.count(rr)) {  // uniform per wave
+        l[u] = lse_at(rr, s);
+        v[u] = res_at(rr, s);
       } else {
         l[u] = -INFINITY;
         v[u] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto load_chunks = [&](int r, int s0, float* l, uint4* v) {  // kSlots == 0: chunks s0, s0 + 4, ...
+  auto load_chunks = [&](int rr, int s0, float* l, uint4* v) {  // kSlots == 0: chunks s0, s0 + 4, ...
+    const int n = rm.count(rr);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int s = s0 + kWaves * u;
-      if (s < splits) {  // uniform per wave
-        l[u] = lse_at(r, s);
-        v[u] = res_at(r, s);
+      if (s < n) {  // uniform per wave
+        l[u] = lse_at(rr, s);
+        v[u] = res_at(rr, s);
       } else {
         l[u] = -INFINITY;
         v[u] = make_uint4(0, 0, 0, 0);
@@ -151,19 +191,9 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
   if (kSlots > 0)
     load_rows(wave * kRowsPerBatch, l_first, v_first);
   else
-    load_chunks(rb, wave, l_first, v_first);
+    load_chunks(0, wave, l_first, v_first);
 
-  // W_UV[head] rows a_base + 16 wave .. + 15 as the A operand: lane (g, l16)
-  // holds row l16, d_c elements 32 s + 8 g .. + 7 for step s.
-  const uint16_t* wrow = w_uv + ((size_t)head * kDh + a_base + 16 * wave + l16) * kDc;
-  bf16x8 wa[kDc / 32];
-#pragma unroll
-  for (int s = 0; s < kDc / 32; ++s)
-    wa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(wrow + 32 * s + 8 * g));
-  // keep the weight loads here, in flight during the merge (the scheduler
-  // would otherwise move them after the merge arithmetic)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+  if (!kPreloaded) load_weights(f, head, a_base, wave, lane, wa);
 
   // ---- combine: c_bar of rows rb .. rb + nr - 1 into LDS ----
   // The prefetched batch is merged on a code path of its own: joined with
@@ -190,8 +220,8 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
     if (row0 < nr) {
       merge_rows(row0, l_first, v_first);
       for (row0 += kWaves * kRowsPerBatch; row0 < nr; row0 += kWaves * kRowsPerBatch) {
-        float l[kBatch];
-        uint4 v[kBatch];
+        float l[kItems];
+        uint4 v[kItems];
         load_rows(row0, l, v);
         merge_rows(row0, l, v);
       }
@@ -202,7 +232,6 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
     // every 4th chunk with its own running maximum, the four are merged
     // through LDS; the first row (prefetched batch) is peeled off the loop
     auto merge_row = [&](int rr, bool prefetched) {
-      const int r = rb + rr;
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       float wsum = 0.f, mx = -INFINITY;
       auto merge_chunks = [&](const float* l, const uint4* v) {
@@ -223,13 +252,13 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
       } else {
         float l[kBatch];
         uint4 v[kBatch];
-        load_chunks(r, wave, l, v);
+        load_chunks(rr, wave, l, v);
         merge_chunks(l, v);
       }
-      for (int s0 = wave + kWaves * kBatch; s0 < splits; s0 += kWaves * kBatch) {
+      for (int s0 = wave + kWaves * kBatch; s0 < rm.count(rr); s0 += kWaves * kBatch) {
         float l[kBatch];
         uint4 v[kBatch];
-        load_chunks(r, s0, l, v);
+        load_chunks(rr, s0, l, v);
         merge_chunks(l, v);
       }
       if (wave > 0) {
@@ -278,22 +307,101 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(const uint16_t* _
       uint2 packed;
       packed.x = pack_bf16x2(acc[0], acc[1]);
       packed.y = pack_bf16x2(acc[2], acc[3]);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = packed;
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(f.out) + o) = packed;
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + o) =
+      *reinterpret_cast<float4*>(static_cast<float*>(f.out) + o) =
           make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }
 
+// kSlots >= 0: the merge variant for a fixed chunking.  kSlots < 0: chosen
+// per work-group from the planned chunk counts of its rows, with the weight
+// rows loaded while those are worked out; the variants kept here (up to 8
+// chunk slots per row, or 8 chunks in flight when the waves share a row)
+// leave room for three work-groups per CU.
+template <bool kBf16Out, int kSlots>
+__global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
+  __shared__ __attribute__((aligned(16))) MergeShared sh;
+
+  // blockIdx.x = head + h * (W_UV half + 2 * row block): congruent mod 8
+  // for one head when h % 8 == 0
+  const int head = blockIdx.x % f.h;
+  const int rest = blockIdx.x / f.h;
+  const int a_base = 64 * (rest & 1);
+  const int rb = kRowBlock * (rest >> 1);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int nr = min(kRowBlock, f.rows - rb);
+  if (nr <= 0) return;  // (the host launches no empty block)
+
+  bf16x8 wa[kDc / 32];
+  if (kSlots < 0) load_weights(f, head, a_base, wave, lane, wa);
+  if (f.slots == 0) {  // planned chunking: first chunk and count of every row
+    if (wave == 0) {
+      const chunks::Lens lens(f.context_lens, f.batch, f.max_len, lane);
+      const int c = chunks::chunk_len(lens, f.plan_target, f.plan_min, f.plan_max, lane);
+      const int my_b = lane < nr ? (rb + lane) / f.n_q : -1;
+      int my_first = 0, my_count = 0, first = 0;
+      for (int b0 = 0; b0 < f.batch; b0 += 64) {
+        const int b = b0 + lane;
+        const int n = b < f.batch ? chunks::ceil_div(lens.at(b), c) : 0;
+        const int incl = chunks::wave_scan(n, lane);
+        const int start = first + incl - n;
+        const int src = my_b - b0;
+        const int s_start = __shfl(start, src & 63, 64), s_n = __shfl(n, src & 63, 64);
+        if (src >= 0 && src < 64) {
+          my_first = s_start;
+          my_count = s_n;
+        }
+        first += __shfl(incl, 63, 64);
+      }
+      int mx = lane < nr ? my_count : 0;
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) mx = max(mx, __shfl_xor(mx, m, 64));
+      if (lane < nr) {
+        sh.row_first[lane] = my_first;
+        sh.row_count[lane] = my_count;
+      }
+      if (lane == 0) sh.max_count = mx;
+    }
+    __syncthreads();
+  }
+  const RowMap rm{(const AS3 int*)sh.row_first, (const AS3 int*)sh.row_count, rb, head, f.n_q, f.h, f.slots};
+  if constexpr (kSlots >= 0) {
+    finish_rows<kBf16Out, (kSlots >= 0 ? kSlots : 0)>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+  } else {
+    const int n = *(const AS3 int*)&sh.max_count;
+    if (n <= 1) finish_rows<kBf16Out, 1, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 2) finish_rows<kBf16Out, 2, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 4) finish_rows<kBf16Out, 4, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 8) finish_rows<kBf16Out, 8, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else finish_rows<kBf16Out, 0, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+  }
+}
+
 template <bool kBf16Out>
 void launch_slots(const DecodeArgs& a, const LaunchCtx& s, dim3 grid, int rows) {
-  const uint16_t* po = static_cast<const uint16_t*>(a.part_o);
-  const uint16_t* w = static_cast<const uint16_t*>(a.w_uv);
+  FinishArgs f;
+  f.part_o = static_cast<const uint16_t*>(a.part_o);
+  f.part_lse = a.part_lse;
+  f.w_uv = static_cast<const uint16_t*>(a.w_uv);
+  f.out = a.out;
+  f.context_lens = a.context_lens;
+  f.rows = rows;
+  f.n_q = a.n_q;
+  f.h = a.h;
+  f.batch = a.batch;
+  f.max_len = a.max_len;
+  f.slots = a.planned ? 0 : a.splits;
+  f.plan_target = a.plan_target;
+  f.plan_min = a.plan_min_chunk;
+  f.plan_max = a.plan_max_chunk;
   const int S = a.splits;
-#define MLA_FINISH(k) \
-  launch_kernel(finish_bf16_kernel<kBf16Out, k>, grid, dim3(kThreads), s, po, a.part_lse, w, a.out, rows, S, a.h)
-  if (S <= 1) MLA_FINISH(1);
+#define MLA_FINISH(k) launch_kernel(finish_bf16_kernel<kBf16Out, k>, grid, dim3(kThreads), s, f)
+  if (a.planned) MLA_FINISH(-1);
+  else if (S <= 1) MLA_FINISH(1);
   else if (S <= 2) MLA_FINISH(2);
   else if (S <= 4) MLA_FINISH(4);
   else if (S <= 8) MLA_FINISH(8);

@@ -13,8 +13,17 @@ namespace mla {
 struct DecodeArgs {
   int batch, n_q, h, d_c, d_r, d_h;
   int page_size, max_pages, num_pages, max_len;
-  int splits;      // chunks per sequence (S)
-  int chunk_len;   // tokens per chunk
+  int splits;      // chunks per sequence (S) of a fixed chunking
+  int chunk_len;   // tokens per chunk of a fixed chunking
+  // Fast path: chunk results are stored per global chunk, [chunks][n_q][h]
+  // [d_c].  planned = 0: chunk g is chunk g % splits of sequence g / splits
+  // (chunks = batch * splits).  planned = 1: the chunk length and every
+  // sequence's chunks come from the context lengths on the device
+  // (chunk_plan.h: about plan_target chunks in all, lengths within
+  // [plan_min_chunk, plan_max_chunk]); chunks bounds their number.
+  int planned = 0;
+  int chunks = 0;
+  int plan_target = 0, plan_min_chunk = 0, plan_max_chunk = 0;
   int in_bf16;     // storage type of q, q_r, caches, weights
   int out_bf16;    // storage type of o
   float scale_log2;  // softmax scale * log2(e)
@@ -31,9 +40,9 @@ struct DecodeArgs {
 
   // workspace carve-up
   void* q_abs;      // [R][h][d_c]      bf16 (fast path) or f32 (general path)
-  void* part_o;     // [R][S][h][d_c]   chunk results already normalised: bf16
-                    //                  (fast path) or f32 (general path)
-  float* part_lse;  // [R][S][h]        f32, base-2 log-sum-exp of each chunk
+  void* part_o;     // chunk results already normalised: bf16 [chunks][n_q][h]
+                    // [d_c] (fast path) or f32 [R][S][h][d_c] (general path)
+  float* part_lse;  // f32 base-2 log-sum-exp of each chunk result, same order
   void* c_bar;      // [R][h][d_c]      f32 (general path only)
 };
 

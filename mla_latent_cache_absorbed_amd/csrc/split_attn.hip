@@ -59,7 +59,7 @@
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.
-#include "common.h"
+#include "chunk_plan.h"
 #include "kernels.h"
 
 namespace mla {
@@ -101,9 +101,10 @@ struct SplitArgs {
   const uint16_t* rope_pool;    // [P][page][64]
   const int32_t* page_table;    // [B][max_pages]
   const int32_t* context_lens;  // [B]
-  uint16_t* part_o;             // [R][S][h][512] bf16
-  float* part_lse;              // [R][S][h]
+  uint16_t* part_o;             // [chunks][n_q][h][512] bf16
+  float* part_lse;              // [chunks][n_q][h]
   int batch, n_q, h, head_groups, splits, chunk_len;
+  int planned, chunks, plan_target, plan_min, plan_max;  // chunk numbering (kernels.h)
   int page_size, max_pages, num_pages, max_len;
   float scale_log2;
 };
@@ -168,22 +169,36 @@ static_assert(sizeof(Shared) <= 160 * 1024, "LDS budget");
 __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs p) {
   __shared__ __attribute__((aligned(16))) Shared sh;
 
-  // ---- which (sequence, chunk, query token, head group) this group owns ----
-  const int sharers = p.n_q * p.head_groups;
-  const int x = blockIdx.x;
-  const int rest = x >> 3;
-  const int unit = (rest / sharers) * 8 + (x & 7);
-  if (unit >= p.batch * p.splits) return;
-  const int k = rest % sharers;
-  const int b = unit / p.splits, split = unit % p.splits;
-  const int m = k / p.head_groups, hgi = k % p.head_groups;
-  const int r = b * p.n_q + m;
-  const int t0 = split * p.chunk_len;
-
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
+
+  // ---- which (global chunk, query token, head group) this group owns ----
+  const int sharers = p.n_q * p.head_groups;
+  const int x = blockIdx.x;
+  const int rest = x >> 3;
+  const int unit = (rest / sharers) * 8 + (x & 7);  // global chunk
+  if (unit >= p.chunks) return;
+  const int k = rest % sharers;
+  const int m = k / p.head_groups, hgi = k % p.head_groups;
+  int b, chunk, clen;  // sequence, chunk within it, chunk length
+  if (p.planned) {  // from the context lengths (every wave alike)
+    const chunks::Lens lens(p.context_lens, p.batch, p.max_len, lane);
+    clen = chunks::chunk_len(lens, p.plan_target, p.plan_min, p.plan_max, lane);
+    chunks::locate(lens, clen, unit, lane, b, chunk);
+    // (wave-uniform values: keep them in scalar registers for the DMAs)
+    clen = __builtin_amdgcn_readfirstlane(clen);
+    b = __builtin_amdgcn_readfirstlane(b);
+    chunk = __builtin_amdgcn_readfirstlane(chunk);
+    if (b < 0) return;  // the call has fewer chunks
+  } else {
+    b = unit / p.splits;
+    chunk = unit % p.splits;
+    clen = p.chunk_len;
+  }
+  const int r = b * p.n_q + m;
+  const int t0 = chunk * clen;
   const bool scorer = wave < kWaves - kAccWaves;
 
   // Pool row of the tile starting at token ts of sequence b (tiles past the
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   // Pool rows of tiles 2.. of the chunk into LDS (every tile that can hold a
   // visible token; all threads share the work, before the first barrier).
   auto fill_tile_rows = [&]() {
-    const int bound = min(p.chunk_len, max(p.max_len - t0, 0));
+    const int bound = min(clen, max(p.max_len - t0, 0));
     const int ntiles_max = (bound + kTile - 1) / kTile;
     for (int i = 2 + tid; i < ntiles_max; i += kThreads) sh.tile_row[i] = tile_pool_row(t0 + i * kTile);
   };
@@ -207,14 +222,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   auto chunk_end = [&](int L) {
     L = L < 0 ? 0 : (L > p.max_len ? p.max_len : L);
     const int vis = max(L - p.n_q + m + 1, 0);
-    return min(t0 + p.chunk_len, vis);
+    return min(t0 + clen, vis);
   };
-  float* pl = p.part_lse + ((size_t)r * p.splits + split) * p.h + hgi * kFastHeadsPerGroup;
+  const size_t res_row = ((size_t)unit * p.n_q + m) * p.h + hgi * kFastHeadsPerGroup;  // [chunk][m][head]
+  float* pl = p.part_lse + res_row;
 
   // The chunk result leaves LDS one 1 KB head row per wave instruction:
-  // [R][S][h][d_c] bf16, each wave storing 8 of the 64 heads.
+  // [chunk][n_q][h][d_c] bf16, each wave storing 8 of the 64 heads.
   auto store_result = [&]() {
-    uint16_t* po = p.part_o + (((size_t)r * p.splits + split) * p.h + hgi * kFastHeadsPerGroup) * kDc;
+    uint16_t* po = p.part_o + res_row * kDc;
 #pragma unroll
     for (int k2 = 0; k2 < kFastHeadsPerGroup / kWaves; ++k2) {
       const int head = (kFastHeadsPerGroup / kWaves) * wave + k2;
@@ -545,13 +561,17 @@ hipError_t launch_split_attn_bf16(const DecodeArgs& a, const LaunchCtx& s) {
   p.head_groups = a.h / kFastHeadsPerGroup;
   p.splits = a.splits;
   p.chunk_len = a.chunk_len;
+  p.planned = a.planned;
+  p.chunks = a.chunks;
+  p.plan_target = a.plan_target;
+  p.plan_min = a.plan_min_chunk;
+  p.plan_max = a.plan_max_chunk;
   p.page_size = a.page_size;
   p.max_pages = a.max_pages;
   p.num_pages = a.num_pages;
   p.max_len = a.max_len;
   p.scale_log2 = a.scale_log2;
-  const int units = a.batch * a.splits;
-  const int groups = ((units + 7) / 8) * 8 * a.n_q * p.head_groups;
+  const int groups = ((a.chunks + 7) / 8) * 8 * a.n_q * p.head_groups;
   launch_kernel(split_attn_bf16_kernel, dim3(groups), dim3(kThreads), s, p);
   return hipGetLastError();
 }

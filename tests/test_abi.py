@@ -97,14 +97,21 @@ def test_workspace_size_and_split_plan(L):
     try:
         for B, n_q, T in [(1, 1, 4096), (1, 1, 131072), (4, 4, 1000), (1, 1, 1), (4, 1, 33)]:
             S, chunk = binding.mla_decode_split_plan(plan, B, n_q, T)
-            assert S >= 1 and chunk >= 1
-            assert chunk % 32 == 0            # whole LDS tiles on the bf16 path
-            assert (S - 1) * chunk < T <= S * chunk
             ws = binding.mla_decode_workspace_size(plan, B, n_q, T)
             R = B * n_q
-            # q_abs (bf16), chunk results (bf16), chunk lse (fp32); the fast
-            # path merges the chunks straight into the up-projection
-            need = R * 128 * 512 * 2 + R * S * 128 * 512 * 2 + R * S * 128 * 4
+            target = 256 // (n_q * 2)  # one work-group per CU, two head groups
+            if B == 1 or target <= 2 * B:  # one sequence, or few chunks each: fixed
+                assert S >= 1 and chunk >= 1
+                assert chunk % 32 == 0            # whole LDS tiles on the bf16 path
+                assert (S - 1) * chunk < T <= S * chunk
+                chunks = B * S
+            else:  # several sequences: planned on the device from the lengths
+                assert (S, chunk) == (0, 0)
+                chunks = max(target, B + -(-B * T // 32768))
+            # q_abs (bf16), chunk results (bf16), chunk lse (fp32) per chunk
+            # and query token; the fast path merges the chunks straight into
+            # the up-projection
+            need = R * 128 * 512 * 2 + chunks * n_q * 128 * 512 * 2 + chunks * n_q * 128 * 4
             assert need <= ws <= need + 3 * 256
         assert binding.mla_decode_workspace_size(plan, 0, 1, 10) == 0
         # invalid shapes give 0 and a reason

@@ -184,6 +184,29 @@ def test_chunk_merge_over_row_blocks(torch, splits):
           "merge over row blocks S=%d" % splits)
 
 
+@pytest.mark.parametrize("h,batch", [(64, 100), (128, 130)])
+def test_many_sequences(torch, h, batch):
+    """More sequences than one scan block of the device chunk plan (100
+    sequences with 64 heads: 256 target chunks), and more than half its
+    target chunk count (130 with 128 heads: a fixed chunking instead)."""
+    rng = np.random.default_rng(206)
+    lens = [int(x) for x in rng.integers(1, 400, size=batch)]
+    wl = inputs.make("ds2_t4k", h=h, batch=batch, lens=("list", lens), shuffled=True, seed=207)
+    dw = _run(wl, torch)
+    assert (dw.split_plan() == (0, 0)) == (h == 64)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "%d sequences" % batch)
+
+
+def test_skewed_batch_gives_the_long_sequence_most_chunks(torch):
+    """One long sequence beside short ones: the device plan gives the long
+    one about a hundred chunks (the many-chunk merge of the finish kernel)
+    and the short ones one each."""
+    wl = inputs.make("ds2_t4k", batch=4, lens=("list", [20000, 100, 37, 3000]), shuffled=True, seed=208)
+    dw = _run(wl, torch)
+    assert dw.split_plan() == (0, 0)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "skewed batch")
+
+
 def test_single_token_context_returns_projected_latent(torch):
     wl = inputs.make("ds2_t4k", lens=("fixed", 1), seed=202)
     dw = _run(wl, torch, out_dtype="f32")

@@ -19,9 +19,9 @@ namespace chunks {
 
 constexpr int kAlign = 32;  // tokens: chunks are whole tiles
 
+__device__ __forceinline__ int clamp_len(int L, int max_len) { return L < 0 ? 0 : (L > max_len ? max_len : L); }
 __device__ __forceinline__ int seq_len(const int32_t* lens, int b, int max_len) {
-  const int L = lens[b];
-  return L < 0 ? 0 : (L > max_len ? max_len : L);
+  return clamp_len(lens[b], max_len);
 }
 
 // The clamped context lengths, read once: lane l keeps that of sequence l;
@@ -31,9 +31,23 @@ struct Lens {
   int batch, max_len, mine;
   __device__ __forceinline__ Lens(const int32_t* p, int batch_, int max_len_, int lane)
       : lens(p), batch(batch_), max_len(max_len_), mine(lane < batch_ ? seq_len(p, lane, max_len_) : 0) {}
-  // length of sequence b = lane + 64 k (k >= 0), as visited by the loops below
-  __device__ __forceinline__ int at(int b) const { return b < 64 ? mine : seq_len(lens, b, max_len); }
+  // with context_lens[lane] already loaded (unclamped)
+  __device__ __forceinline__ Lens(const int32_t* p, int batch_, int max_len_, int lane, int raw)
+      : lens(p), batch(batch_), max_len(max_len_), mine(lane < batch_ ? clamp_len(raw, max_len_) : 0) {}
+  // Sum over the sequences of fn(length): lane l takes sequences l, l + 64,
+  // ... (the first from the register), then the wave adds up.
+  template <typename Fn>
+  __device__ __forceinline__ int sum(Fn fn, int lane) const;
 };
+
+__device__ __forceinline__ int wave_sum(int v);
+
+template <typename Fn>
+__device__ __forceinline__ int Lens::sum(Fn fn, int lane) const {
+  int acc = lane < batch ? fn(mine) : 0;
+  for (int b = lane + 64; b < batch; b += 64) acc += fn(seq_len(lens, b, max_len));
+  return wave_sum(acc);
+}
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -55,9 +69,7 @@ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; 
 
 // Chunks of all sequences for chunk length c (wave-uniform).
 __device__ __forceinline__ int count_chunks(const Lens& L, int c, int lane) {
-  int n = 0;
-  for (int b = lane; b < L.batch; b += 64) n += ceil_div(L.at(b), c);
-  return wave_sum(n);
+  return L.sum([c](int len) { return ceil_div(len, c); }, lane);
 }
 
 // The chunk length of the call: about the shortest whole-tile length in
@@ -66,9 +78,7 @@ __device__ __forceinline__ int count_chunks(const Lens& L, int c, int lane) {
 // to whole chunks; target > batch guarantees the last try.
 __device__ __forceinline__ int chunk_len(const Lens& L, int target, int min_len, int max_chunk, int lane) {
   const int batch = L.batch;
-  int total = 0;
-  for (int b = lane; b < batch; b += 64) total += L.at(b);
-  total = wave_sum(total);
+  const int total = L.sum([](int len) { return len; }, lane);
   auto len_for = [&](int parts) {
     int c = ceil_div(ceil_div(total, parts > 0 ? parts : 1), kAlign) * kAlign;
     return c < min_len ? min_len : (c > max_chunk ? max_chunk : c);
@@ -93,7 +103,7 @@ __device__ __forceinline__ void locate(const Lens& L, int c, int g, int lane, in
   int first = 0;
   for (int b0 = 0; b0 < L.batch; b0 += 64) {
     const int b = b0 + lane;
-    const int n = b < L.batch ? ceil_div(L.at(b), c) : 0;
+    const int n = b < L.batch ? ceil_div(b0 == 0 ? L.mine : seq_len(L.lens, b, L.max_len), c) : 0;
     const int incl = wave_scan(n, lane);
     const int start = first + incl - n;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(b < L.batch && g >= start && g < start + n);

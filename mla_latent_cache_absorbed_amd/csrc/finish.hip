@@ -336,17 +336,21 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
   const int nr = min(kRowBlock, f.rows - rb);
   if (nr <= 0) return;  // (the host launches no empty block)
 
+  // planned chunking: the lengths go out first, the weight rows behind them
+  // (loads complete in order), then the first chunk and count of every row
+  int my_len = 0;
+  if (kSlots < 0 && wave == 0 && lane < f.batch) my_len = f.context_lens[lane];
   bf16x8 wa[kDc / 32];
   if (kSlots < 0) load_weights(f, head, a_base, wave, lane, wa);
-  if (f.slots == 0) {  // planned chunking: first chunk and count of every row
+  if (f.slots == 0) {
     if (wave == 0) {
-      const chunks::Lens lens(f.context_lens, f.batch, f.max_len, lane);
+      const chunks::Lens lens(f.context_lens, f.batch, f.max_len, lane, my_len);
       const int c = chunks::chunk_len(lens, f.plan_target, f.plan_min, f.plan_max, lane);
       const int my_b = lane < nr ? (rb + lane) / f.n_q : -1;
       int my_first = 0, my_count = 0, first = 0;
       for (int b0 = 0; b0 < f.batch; b0 += 64) {
         const int b = b0 + lane;
-        const int n = b < f.batch ? chunks::ceil_div(lens.at(b), c) : 0;
+        const int n = b < f.batch ? chunks::ceil_div(b0 == 0 ? lens.mine : chunks::seq_len(f.context_lens, b, f.max_len), c) : 0;
         const int incl = chunks::wave_scan(n, lane);
         const int start = first + incl - n;
         const int src = my_b - b0;

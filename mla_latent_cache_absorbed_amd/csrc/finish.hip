@@ -27,9 +27,10 @@
 // operand.  Work-groups of one head get block indices congruent mod 8, so
 // they run on one XCD and the W_UV rows and chunk results that several of
 // them read come from its L2.  Two ways to merge:
-// - few chunks (S <= 16): each wave merges whole query rows on its own,
-//   every (row, chunk) load of a batch in flight at once;
-// - many chunks: all four waves merge one row, each with every fourth chunk
+// - few chunks (S <= 16) and at least four rows: each wave merges whole
+//   query rows on its own, every (row, chunk) load of a batch in flight at
+//   once;
+// - otherwise all four waves merge one row, each with every fourth chunk
 //   and its own running maximum, and the four partial sums meet in LDS.
 #include "chunk_plan.h"
 #include "kernels.h"
@@ -377,7 +378,8 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
     finish_rows<kBf16Out, (kSlots >= 0 ? kSlots : 0)>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
   } else {
     const int n = *(const AS3 int*)&sh.max_count;
-    if (n <= 1) finish_rows<kBf16Out, 1, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    if (nr < kWaves && n > 1) finish_rows<kBf16Out, 0, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 1) finish_rows<kBf16Out, 1, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
     else if (n <= 2) finish_rows<kBf16Out, 2, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
     else if (n <= 4) finish_rows<kBf16Out, 4, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
     else if (n <= 8) finish_rows<kBf16Out, 8, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
@@ -405,6 +407,7 @@ void launch_slots(const DecodeArgs& a, const LaunchCtx& s, dim3 grid, int rows) 
   const int S = a.splits;
 #define MLA_FINISH(k) launch_kernel(finish_bf16_kernel<kBf16Out, k>, grid, dim3(kThreads), s, f)
   if (a.planned) MLA_FINISH(-1);
+  else if (rows < kWaves && S > 1) MLA_FINISH(0);  // too few rows to give every wave its own
   else if (S <= 1) MLA_FINISH(1);
   else if (S <= 2) MLA_FINISH(2);
   else if (S <= 4) MLA_FINISH(4);

@@ -1,8 +1,10 @@
 // decode.cpp -- host side of the C ABI in include/mla_decode.h.
 //
 // Validates configurations and calls, chooses how the context is split into
-// chunks, carves the caller's workspace, and enqueues the four kernels on the
-// caller's stream.  It never allocates device memory and never synchronises.
+// chunks (or that the kernels plan it from the context lengths), carves the
+// caller's workspace, and enqueues the kernels on the caller's stream: three
+// on the bf16 fast path, four on the general path.  It never allocates device
+// memory and never synchronises.
 #include "mla_decode.h"
 
 #include <hip/hip_runtime.h>

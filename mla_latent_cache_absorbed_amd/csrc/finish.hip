@@ -1,8 +1,8 @@
 // finish.hip -- split combine and W_UV up-projection in one pass (fast path).
 //
 // For query row r and head i the split kernel left one normalised latent
-// o_s (bf16, [R][S][h][512]) and one base-2 log-sum-exp lse_s (fp32) per
-// context chunk s.  This kernel forms
+// o_s (bf16) and one base-2 log-sum-exp lse_s (fp32) per context chunk s of
+// the row's sequence.  This kernel forms
 //   c_bar = sum_s w_s o_s / sum_s w_s,   w_s = 2^(lse_s - m)
 // for any reference m (here the maximum, or running maxima merged at the
 // end) (the softmax over the whole visible context evaluated chunk by

@@ -59,6 +59,12 @@
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.
+// - Chunks are numbered over the whole batch (one work-group per chunk,
+//   query token and head group) and their results stored [chunk][n_q][h]
+//   [d_c].  Either every sequence has the same number of chunks, or the
+//   chunk length is planned from the context lengths (chunk_plan.h) and
+//   each work-group finds its sequence and chunk by a scan of the lengths,
+//   so that ragged batches keep every work-group about equally long.
 #include "chunk_plan.h"
 #include "kernels.h"
 

@@ -21,6 +21,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -37,14 +38,22 @@ KERNELS = {
 }
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and blank space (the kernel sources hold
+    no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel: str) -> str:
-    """Digest of the files that determine one kernel's code (its source and
-    every shared header)."""
+    """Digest of the code that determines one kernel (its source and every
+    shared header, comments and layout ignored)."""
     h = hashlib.sha256()
     headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
     for f in [KERNELS[kernel][1]] + headers:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -93,8 +93,8 @@ mla_status_t mla_decode_create(const mla_decode_config_t* cfg, mla_decode_t* out
 
 /* Bytes of device workspace `run` needs for this batch shape (0 on an
  * invalid request; the reason is in mla_decode_last_error()).  The
- * workspace holds the absorbed queries, the per-chunk partial results and
- * log-sum-exps, and the merged latents. */
+ * workspace holds the absorbed queries and the per-chunk partial results
+ * and log-sum-exps (and, on the general path, the merged latents). */
 size_t mla_decode_workspace_size(mla_decode_t plan, int32_t batch, int32_t n_q,
                                  int32_t max_context_len);
 

@@ -73,20 +73,21 @@ struct FinishArgs {
 
 // Where the chunk results of the rows of one block are: lse index of chunk 0
 // of row rb + rr (this head), the index step from one chunk to the next, and
-// the row's number of chunks.
+// the row's number of chunks, for the fixed chunking or the planned one.
 // (The planned tables are read through LDS pointers: a generic pointer
 // would make the compiler wait for every global load in flight.)
+template <bool kPlanned>
 struct RowMap {
   const AS3 int* first;  // planned: row_first, row_count in LDS
   const AS3 int* count_;
   int rb, head, n_q, h, slots;
   __device__ __forceinline__ size_t base(int rr) const {
     const int r = rb + rr, b = r / n_q, m = r - b * n_q;
-    const int g0 = slots > 0 ? b * slots : first[rr];
+    const int g0 = kPlanned ? first[rr] : b * slots;
     return ((size_t)g0 * n_q + m) * h + head;
   }
   __device__ __forceinline__ size_t step() const { return (size_t)n_q * h; }
-  __device__ __forceinline__ int count(int rr) const { return slots > 0 ? slots : count_[rr]; }
+  __device__ __forceinline__ int count(int rr) const { return kPlanned ? count_[rr] : slots; }
 };
 
 // Weighted sum of one batch of chunk results into (acc0, acc1, wsum) with
@@ -144,8 +145,8 @@ __device__ __forceinline__ void load_weights(const FinishArgs& f, int head, int 
 
 // kPreloaded: the caller has loaded the weight rows into wa already.
 // kBatch: chunk loads in flight per lane when the waves share a row.
-template <bool kBf16Out, int kSlots, bool kPreloaded = false, int kBatch = kMergeBatch>
-__device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh, const RowMap& rm, int head,
+template <bool kBf16Out, int kSlots, bool kPreloaded, int kBatch, typename Map>
+__device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh, const Map& rm, int head,
                                             int a_base, int rb, int nr, int wave, int lane, bf16x8* wa) {
   const int h = f.h;
   const int g = lane >> 4, l16 = lane & 15;
@@ -316,12 +317,13 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
   }
 }
 
-// kSlots >= 0: the merge variant for a fixed chunking.  kSlots < 0: chosen
-// per work-group from the planned chunk counts of its rows, with the weight
-// rows loaded while those are worked out; the variants kept here (up to 8
-// chunk slots per row, or 8 chunks in flight when the waves share a row)
-// leave room for three work-groups per CU.
-template <bool kBf16Out, int kSlots>
+// kSlots >= 0: the merge variant for a fixed chunking, kBatch chunks in
+// flight per lane when the waves share a row.  kSlots < 0: planned
+// chunking, the variant chosen per work-group from the chunk counts of its
+// rows, with the weight rows loaded while those are worked out; the
+// variants kept here (up to 8 chunk slots per row, or 8 chunks in flight
+// when the waves share a row) leave room for three work-groups per CU.
+template <bool kBf16Out, int kSlots, int kBatch>
 __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
   __shared__ __attribute__((aligned(16))) MergeShared sh;
 
@@ -336,14 +338,18 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
   const int lane = tid & 63;
   const int nr = min(kRowBlock, f.rows - rb);
   if (nr <= 0) return;  // (the host launches no empty block)
-
-  // planned chunking: the lengths go out first, the weight rows behind them
-  // (loads complete in order), then the first chunk and count of every row
-  int my_len = 0;
-  if (kSlots < 0 && wave == 0 && lane < f.batch) my_len = f.context_lens[lane];
   bf16x8 wa[kDc / 32];
-  if (kSlots < 0) load_weights(f, head, a_base, wave, lane, wa);
-  if (f.slots == 0) {
+
+  if constexpr (kSlots >= 0) {
+    const RowMap<false> rm{nullptr, nullptr, rb, head, f.n_q, f.h, f.slots};
+    finish_rows<kBf16Out, (kSlots >= 0 ? kSlots : 0), false, kBatch>(f, sh, rm, head, a_base, rb, nr, wave,
+                                                                     lane, wa);
+  } else {
+    // the lengths go out first, the weight rows behind them (loads
+    // complete in order), then the first chunk and count of every row
+    int my_len = 0;
+    if (wave == 0 && lane < f.batch) my_len = f.context_lens[lane];
+    load_weights(f, head, a_base, wave, lane, wa);
     if (wave == 0) {
       const chunks::Lens lens(f.context_lens, f.batch, f.max_len, lane, my_len);
       const int c = chunks::chunk_len(lens, f.plan_target, f.plan_min, f.plan_max, lane);
@@ -372,17 +378,13 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
       if (lane == 0) sh.max_count = mx;
     }
     __syncthreads();
-  }
-  const RowMap rm{(const AS3 int*)sh.row_first, (const AS3 int*)sh.row_count, rb, head, f.n_q, f.h, f.slots};
-  if constexpr (kSlots >= 0) {
-    finish_rows<kBf16Out, (kSlots >= 0 ? kSlots : 0)>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
-  } else {
+    const RowMap<true> rm{(const AS3 int*)sh.row_first, (const AS3 int*)sh.row_count, rb, head, f.n_q, f.h, 0};
     const int n = *(const AS3 int*)&sh.max_count;
     if (nr < kWaves && n > 1) finish_rows<kBf16Out, 0, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
-    else if (n <= 1) finish_rows<kBf16Out, 1, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
-    else if (n <= 2) finish_rows<kBf16Out, 2, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
-    else if (n <= 4) finish_rows<kBf16Out, 4, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
-    else if (n <= 8) finish_rows<kBf16Out, 8, true>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 1) finish_rows<kBf16Out, 1, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 2) finish_rows<kBf16Out, 2, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 4) finish_rows<kBf16Out, 4, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
+    else if (n <= 8) finish_rows<kBf16Out, 8, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
     else finish_rows<kBf16Out, 0, true, 8>(f, sh, rm, head, a_base, rb, nr, wave, lane, wa);
   }
 }
@@ -405,15 +407,16 @@ void launch_slots(const DecodeArgs& a, const LaunchCtx& s, dim3 grid, int rows) 
   f.plan_min = a.plan_min_chunk;
   f.plan_max = a.plan_max_chunk;
   const int S = a.splits;
-#define MLA_FINISH(k) launch_kernel(finish_bf16_kernel<kBf16Out, k>, grid, dim3(kThreads), s, f)
-  if (a.planned) MLA_FINISH(-1);
-  else if (rows < kWaves && S > 1) MLA_FINISH(0);  // too few rows to give every wave its own
-  else if (S <= 1) MLA_FINISH(1);
-  else if (S <= 2) MLA_FINISH(2);
-  else if (S <= 4) MLA_FINISH(4);
-  else if (S <= 8) MLA_FINISH(8);
-  else if (S <= 16) MLA_FINISH(16);
-  else MLA_FINISH(0);
+#define MLA_FINISH(k, n) launch_kernel(finish_bf16_kernel<kBf16Out, k, n>, grid, dim3(kThreads), s, f)
+  if (a.planned) MLA_FINISH(-1, 8);
+  else if (S <= 1) MLA_FINISH(1, 16);
+  else if (rows >= kWaves && S <= 16) {  // every wave merges rows of its own
+    if (S <= 2) MLA_FINISH(2, 16);
+    else if (S <= 4) MLA_FINISH(4, 16);
+    else if (S <= 8) MLA_FINISH(8, 16);
+    else MLA_FINISH(16, 16);
+  } else if (S <= kWaves * 8) MLA_FINISH(0, 8);  // the waves share each row
+  else MLA_FINISH(0, 16);
 #undef MLA_FINISH
 }
 

@@ -97,7 +97,6 @@ static_assert(kBlocks == 4 && kTile == 32, "load mapping assumes 4 head blocks a
 // the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
 constexpr float kRescaleSlack = 8.0f;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct SplitArgs {

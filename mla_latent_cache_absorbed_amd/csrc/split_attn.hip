@@ -93,6 +93,12 @@ constexpr int kScoreReadsAhead = 6;
 constexpr int kAccReadsAhead = 6;
 
 static_assert(kBlocks == 4 && kTile == 32, "load mapping assumes 4 head blocks and 32-token tiles");
+// The absorbed query of the group (64 rows of 1 KB, then 64 RoPE rows of
+// 128 B) passes through ring stages kQStage.. during the prologue.
+constexpr int kQStage = 2;
+constexpr int kQLatBytes = kFastHeadsPerGroup * kDc * 2;
+static_assert(kQLatBytes + kFastHeadsPerGroup * kDr * 2 <= (kStages - kQStage) * kStageBytes,
+              "the query fits into the ring stages that the prologue leaves free");
 // Largest factor (as a power of two) by which a weight may exceed 1 before
 // the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
 constexpr float kRescaleSlack = 8.0f;
@@ -283,40 +289,41 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   // barrier it + 1.  Each role keeps all of its state inside its own branch,
   // so that nothing of one role is live across the other's loop.
   if (scorer) {
-    // ---- prologue: the length, the first tiles' and the other tiles' pool
-    //      rows and the absorbed query go out together ----
+    // ---- prologue: this wave's 16 absorbed-query rows (and their RoPE
+    //      parts) come into ring stages 2-3 by DMA, whole 1 KB rows per
+    //      instruction, with the tile-row swizzles; the length and the other
+    //      tiles' pool rows go out behind them ----
+    const int blk = wave;  // head block within the group
+    const int head0 = hgi * kFastHeadsPerGroup + 16 * blk;  // first head of the block
+    const uint32_t q_lds = ring_base + (uint32_t)(kQStage * kStageBytes);
+    {
+      const uint8_t* qa_src = reinterpret_cast<const uint8_t*>(p.q_abs + ((size_t)r * p.h + head0) * kDc);
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        lds_dma16(qa_src + (size_t)j * (kDc * 2), 16u * (uint32_t)(lane ^ lat_swz(j)),
+                  q_lds + (uint32_t)(16 * blk + j) * (kDc * 2));
+      const uint8_t* qr_src = reinterpret_cast<const uint8_t*>(p.q_r + ((size_t)r * p.h + head0) * kDr);
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int row = 8 * d + (lane >> 3);  // head within the block
+        lds_dma16(qr_src + (size_t)(8 * d) * (kDr * 2),
+                  (uint32_t)(lane >> 3) * (kDr * 2) + 16u * (uint32_t)((lane & 7) ^ rope_swz(row)),
+                  q_lds + (uint32_t)kQLatBytes + (uint32_t)(16 * blk + 8 * d) * (kDr * 2));
+      }
+    }
     const int L = p.context_lens[b];
     fill_tile_rows();
-    const int blk = wave;  // head block within the group
-    const int head = hgi * kFastHeadsPerGroup + 16 * blk + l16;
-    bf16x8 qa[kDc / 32], qr[kDr / 32];
-    {
-      const uint16_t* qa_row = p.q_abs + ((size_t)r * p.h + head) * kDc;
-      const uint16_t* qr_row = p.q_r + ((size_t)r * p.h + head) * kDr;
-#pragma unroll
-      for (int s = 0; s < kDc / 32; ++s)
-        qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qa_row + 32 * s + 8 * g));
-#pragma unroll
-      for (int s = 0; s < kDr / 32; ++s)
-        qr[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qr_row + 32 * s + 8 * g));
-    }
     const int t1 = chunk_end(L);
     if (t0 >= t1) {  // nothing visible: lse = -inf, the chunk result is never read
       if (g == 0) pl[16 * blk + l16] = -INFINITY;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no DMA outlives the work-group
       return;
     }
     const int ntiles = (t1 - t0 + kTile - 1) / kTile;
-    // Consume the query registers here, so that the compiler's own waits for
-    // them stay out of the loop.
-#pragma unroll
-    for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
-#pragma unroll
-    for (int s = 0; s < kDr / 32; ++s) asm volatile("" :: "v"(qr[s]));
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // tile_row is visible, the first tiles are in LDS
 
     // score reads: row l16 (+16 tb), chunk 4s + g -> (4s) ^ c1_x with
-    // c1_x = g ^ lat_swz(l16) < 16, i.e. base[s & 3] + 256 (s >> 2)
+    // c1_x = g ^ lat_swz(l16) < 16, i.e. base[s & 3] + 256 (s >> 2); the
+    // query rows of the block sit in the same layout
     const int c1_x = g ^ lat_swz(l16);
     const int rope_x = g ^ rope_swz(l16);
     uint32_t c1_base[4], rope_base[2];
@@ -324,6 +331,27 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     for (int k2 = 0; k2 < 4; ++k2) c1_base[k2] = l16 * (kDc * 2) + 16 * ((4 * k2) ^ c1_x);
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) rope_base[k2] = kLatBytes + l16 * (kDr * 2) + 16 * ((4 * k2) ^ rope_x);
+
+    // this wave's DMAs have landed: the query operands into registers, read
+    // before the barrier after which stage 2 takes tile 2
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const AS3 uint8_t* q_blk = (const AS3 uint8_t*)sh.ring + kQStage * kStageBytes + 16 * blk * (kDc * 2);
+    const AS3 uint8_t* qr_blk = (const AS3 uint8_t*)sh.ring + kQStage * kStageBytes + kQLatBytes +
+                                16 * blk * (kDr * 2) - kLatBytes;
+    bf16x8 qa[kDc / 32], qr[kDr / 32];
+#pragma unroll
+    for (int s = 0; s < kDc / 32; ++s)
+      qa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(q_blk + c1_base[s & 3] + 256 * (s >> 2)));
+#pragma unroll
+    for (int s = 0; s < kDr / 32; ++s)
+      qr[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const AS3 u32x4*>(qr_blk + rope_base[s]));
+    // Consume the query registers here, so that the compiler's own waits for
+    // them stay out of the loop.
+#pragma unroll
+    for (int s = 0; s < kDc / 32; ++s) asm volatile("" :: "v"(qa[s]));
+#pragma unroll
+    for (int s = 0; s < kDr / 32; ++s) asm volatile("" :: "v"(qr[s]));
+    __syncthreads();  // tile_row is visible, the first tiles are in LDS, the query is read
 
     float m_run = -INFINITY, l_run = 0.f;  // reference maximum, per-lane partial weight sum
     for (int it = 0; it < ntiles; ++it) {

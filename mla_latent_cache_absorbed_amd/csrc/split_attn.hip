@@ -559,16 +559,20 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     }
   }
   block_barrier();  // pairs with the score waves' barrier after their lse
-  // normalised result (bf16) into LDS, head-major, then out by all waves
+  // normalised result (bf16) into LDS, head-major, then out by all waves;
+  // head 16 hb + l16 differs from head l16 by hb * 16 rows (the swizzle
+  // depends on the head mod 16 only), an immediate offset
+  uint32_t w_ofs[kAccFeatureBlocks];
+#pragma unroll
+  for (int fbl = 0; fbl < kAccFeatureBlocks; ++fbl)
+    w_ofs[fbl] = result_offset(l16, 16 * (kAccFeatureBlocks * a + fbl) + 4 * g);  // D[4g + j][l16]
 #pragma unroll
   for (int hb = 0; hb < kBlocks; ++hb) {
     const float inv = sh.inv_l[16 * hb + l16];
-    const int head = 16 * hb + l16;
 #pragma unroll
     for (int fbl = 0; fbl < kAccFeatureBlocks; ++fbl) {
-      const int f0 = 16 * (kAccFeatureBlocks * a + fbl) + 4 * g;  // D[4g + j][l16]
       const f32x4 v = acc[fbl][hb] * inv;
-      *reinterpret_cast<AS3 u32x2*>((AS3 uint8_t*)sh.ring + result_offset(head, f0)) =
+      *reinterpret_cast<AS3 u32x2*>((AS3 uint8_t*)sh.ring + w_ofs[fbl] + hb * 16 * (kDc * 2)) =
           u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
     }
   }

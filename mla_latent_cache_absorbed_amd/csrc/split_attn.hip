@@ -161,10 +161,16 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // Chunk result, head-major in the (then free) tile ring: head row of 1 KB,
-// its 32-byte granules XOR-swizzled by the head so that the accumulate
-// waves' 8-byte writes (16 heads x 32 bytes each) spread over the banks.
+// its 16-byte chunks XOR-swizzled by head bits 0-3 and the two 8-byte
+// halves of each chunk by head bit 3.  An accumulate-wave write stores
+// 8 bytes (4 features) per lane for 16 heads; with both swizzles every 16
+// lanes of it hit 16 different 8-byte bank pairs of a 128-byte line (the
+// earlier 32-byte swizzle alone left 4 per line: a 4-way conflict, 12
+// extra cycles per write instruction by the SQ_LDS_BANK_CONFLICT counter).
+// A reader of whole chunks swaps the halves back when head bit 3 is set.
 __device__ __forceinline__ uint32_t result_offset(int head, int feature) {
-  return (uint32_t)head * (kDc * 2) + 32u * (uint32_t)((feature >> 4) ^ (head & 15)) + 2u * (feature & 15);
+  return (uint32_t)head * (kDc * 2) + 16u * (uint32_t)((feature >> 3) ^ (head & 15)) +
+         8u * (uint32_t)(((feature >> 2) & 1) ^ ((head >> 3) & 1)) + 2u * (feature & 3);
 }
 
 struct Shared {
@@ -245,7 +251,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
 #pragma unroll
     for (int k2 = 0; k2 < kFastHeadsPerGroup / kWaves; ++k2) {
       const int head = (kFastHeadsPerGroup / kWaves) * wave + k2;
-      const u32x4 v = *reinterpret_cast<const AS3 u32x4*>((AS3 uint8_t*)sh.ring + result_offset(head, 8 * lane));
+      // features 8 lane .. 8 lane + 7: one chunk, its halves swapped for
+      // head bit 3
+      const u32x4 c = *reinterpret_cast<const AS3 u32x4*>((AS3 uint8_t*)sh.ring + head * (kDc * 2) +
+                                                          16 * (lane ^ (head & 15)));
+      const u32x4 v = (head & 8) ? u32x4{c[2], c[3], c[0], c[1]} : c;
       *reinterpret_cast<u32x4*>(po + (size_t)head * kDc + 8 * lane) = v;
     }
   };

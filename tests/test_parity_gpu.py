@@ -197,6 +197,19 @@ def test_many_sequences(torch, h, batch):
     check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "%d sequences" % batch)
 
 
+@pytest.mark.parametrize("splits", [0, 3])
+def test_four_head_groups_two_query_tokens(torch, splits):
+    """h = 256 (four 64-head groups, each with its own query rows in the
+    split kernel's prologue) and two query tokens per sequence, ragged
+    paged contexts: every (chunk, token, head group) work-group stages a
+    different slice of the absorbed query."""
+    wl = inputs.make("ds2_mtp_b16", h=256, n_q=2, batch=3, lens=("list", [70, 333, 190]),
+                     shuffled=True, seed=209)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16",
+          "h=256 n_q=2 S=%d" % splits)
+
+
 def test_skewed_batch_gives_the_long_sequence_most_chunks(torch):
     """One long sequence beside short ones: the device plan gives the long
     one about a hundred chunks (the many-chunk merge of the finish kernel)

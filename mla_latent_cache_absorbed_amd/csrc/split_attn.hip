@@ -294,9 +294,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   // written by the score waves between barriers k and k + 1, read by the
   // accumulate waves between barriers k + 1 and k + 2, and overwritten
   // (tile k + 2) only after that.  The accumulate waves issue tile it + 2
-  // right after barrier it, into the stage that tile it - 2 (finished before
-  // that barrier) occupied, and wait for their share of tile it + 1 before
-  // barrier it + 1.  Each role keeps all of its state inside its own branch,
+  // between barriers it and it + 1 (after folding tile it - 1), into the
+  // stage that tile it - 2 (finished before barrier it) occupied, and wait
+  // for their share of tile it + 1 before barrier it + 1.  Each role keeps all of its state inside its own branch,
   // so that nothing of one role is live across the other's loop.
   if (scorer) {
     // ---- prologue: this wave's 16 absorbed-query rows (and their RoPE
@@ -532,8 +532,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       return as_bf16x8(v);
     };
     // The four rescale flags, P(j) and the first latent operands go out
-    // together; the tile DMAs are issued while they land (a DMA holds the
-    // wave at issue), and the MFMAs follow.
+    // together and the MFMAs follow; the tile DMAs come last (a DMA holds
+    // the wave at issue while the CU's fetch path is busy, which at the
+    // start of the iteration delayed the MFMAs; at the end it overlaps the
+    // score waves' softmax).
     const u32x4 flags = sh.rescale[slot];
     bf16x8 pb[kBlocks];
 #pragma unroll
@@ -542,10 +544,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     bf16x8 opq[kAhead + 1];
 #pragma unroll
     for (int fb = 0; fb < kAhead; ++fb) opq[fb] = latent_operand(fb);
-    if (more) {
-#pragma unroll
-      for (int part = 0; part < kAccDmas; ++part) dma(it + 2, row_next, t1, part, lat_voff);
-    }
     if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {  // the reference maximum moved (rare)
 #pragma unroll
       for (int hb = 0; hb < kBlocks; ++hb) {
@@ -566,6 +564,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       for (int hb = 0; hb < kBlocks; ++hb)
         acc[fb][hb] = mfma16x16x32(opq[fb % (kAhead + 1)], pb[hb], acc[fb][hb]);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) {
+#pragma unroll
+      for (int part = 0; part < kAccDmas; ++part) dma(it + 2, row_next, t1, part, lat_voff);
     }
   }
   block_barrier();  // pairs with the score waves' barrier after their lse

@@ -24,8 +24,9 @@
  * Conventions
  *   - All device buffers are caller-owned (typically torch tensors); the
  *     library owns only the opaque host-side plan.  `run` never allocates,
- *     frees or synchronises: it enqueues four kernels on the caller's stream
- *     and returns.
+ *     frees or synchronises: it enqueues its kernels on the caller's stream
+ *     (three on the bf16 fast path, where the merge and the up-projection
+ *     are one kernel; four on the general path) and returns.
  *   - Layouts are dense row-major with the listed shapes.  Weights act on
  *     column vectors: k = W_UK[i] c, with W[i] a d_h x d_c matrix.
  *   - `context_lens[b]` counts every cached token of sequence b, including
@@ -132,7 +133,7 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing (instrumentation, off by default).  With max_runs > 0
- * every later `run` on this plan launches each of its four kernels (absorb,
+ * every later `run` on this plan launches each of its kernels (absorb,
  * split, combine, up-project) with a start and a stop HIP event that the
  * dispatch itself fills in (the kernel's own begin and end, as a profiler
  * sees them, not the gaps between launches), for up to max_runs runs;

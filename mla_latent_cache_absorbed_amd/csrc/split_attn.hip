@@ -486,8 +486,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
 #pragma unroll
     for (int part = 0; part < kAccDmas; ++part) dma(1, row_b, t1, part, lat_voff);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();  // tile_row is visible, the first tiles are in LDS
+  // tile 0 has landed (tile 1 may still be in flight: the loop waits for
+  // it before barrier 1)
+  if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // tile_row is visible, tile 0 is in LDS
 
   // transposing reads: row 4g + e (+16 for the upper 16 tokens), chunk
   // 2 fb + (q >> 1), half q & 1 -> base[fb & 7] + 256 (fb >> 3)

@@ -103,8 +103,6 @@ static_assert(kQLatBytes + kFastHeadsPerGroup * kDr * 2 <= (kStages - kQStage) *
 // the reference maximum moves; 2^8 keeps every sum far from fp32 overflow.
 constexpr float kRescaleSlack = 8.0f;
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 struct SplitArgs {
   const uint16_t* q_abs;        // [R][h][512]
   const uint16_t* q_r;          // [R][h][64]

@@ -210,6 +210,18 @@ def test_four_head_groups_two_query_tokens(torch, splits):
           "h=256 n_q=2 S=%d" % splits)
 
 
+@pytest.mark.parametrize("page_size,splits", [(32, 0), (32, 5), (256, 0), (256, 3)])
+def test_page_sizes(torch, page_size, splits):
+    """Pages of one tile (32 tokens) and of eight (256): the fast path's
+    tiles never straddle a page, and every page-table lookup (per tile, in
+    LDS) lands on the right page of a shuffled pool."""
+    wl = inputs.make("ds2_t4k", batch=3, page_size=page_size, lens=("list", [33, 700, 257]),
+                     shuffled=True, seed=210 + page_size)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16",
+          "page size %d S=%d" % (page_size, splits))
+
+
 def test_skewed_batch_gives_the_long_sequence_most_chunks(torch):
     """One long sequence beside short ones: the device plan gives the long
     one about a hundred chunks (the many-chunk merge of the finish kernel)

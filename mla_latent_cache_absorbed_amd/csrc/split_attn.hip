@@ -32,13 +32,16 @@
 //   filled by direct global->LDS DMA (global_load_lds_dwordx4): no staging
 //   registers; tiles k+1 and k+2 are in flight while the score waves read
 //   tile k and the accumulate waves tile k-1.  A DMA instruction holds its
-//   wave at issue for a while, so the accumulate waves issue them while the
-//   score waves' MFMAs run, and run their own MFMAs while the score waves
-//   do the softmax arithmetic.  A tile never straddles a
-//   cache page (pages are multiples of 32 tokens), so each tile is one
-//   contiguous run of 32 latent rows and 32 RoPE rows in the pool; every
-//   tile's pool row is looked up once at the start, in parallel with the
-//   context length and the query loads.
+//   wave at issue while the CU's fetch path is busy, so the accumulate
+//   waves issue a tile's DMAs after their MFMAs, while the score waves do
+//   the softmax arithmetic.  A tile never straddles a cache page (pages are
+//   multiples of 32 tokens), so each tile is one contiguous run of 32
+//   latent rows and 32 RoPE rows in the pool; every tile's pool row is
+//   looked up once at the start.
+// - Prologue: the group's absorbed-query rows (64 x 1 KB, plus their RoPE
+//   parts) come into the two ring stages that tiles 2 and 3 will use, by
+//   DMA in whole rows, and the score waves read their operands from there;
+//   the first barrier waits for tile 0 only.
 // - The tile stays token-major in LDS with its 16-byte chunks XOR-swizzled
 //   per row, so that both read patterns below are free of bank conflicts.
 // - Scores: S^T[token][head] = KV[token][:] . Q[head][:], tokens as M, heads
@@ -55,7 +58,8 @@
 //   matching B-operand order, so it crosses LDS as one 16-byte store and load
 //   per lane and head block.
 // - The chunk result is transposed to head-major order through the (by then
-//   free) LDS ring, so that every wave stores whole 1 KB head rows.
+//   free) LDS ring, so that every wave stores whole 1 KB head rows, with
+//   non-temporal stores.
 // - Work-groups that read the same chunk (other heads, other query tokens of
 //   the same sequence) get block indices congruent mod 8, so they run on one
 //   XCD and share its L2.

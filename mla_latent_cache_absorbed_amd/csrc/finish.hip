@@ -90,15 +90,23 @@ struct RowMap {
   __device__ __forceinline__ int count(int rr) const { return kPlanned ? count_[rr] : slots; }
 };
 
+// Value of v in lane u (u uniform), as a scalar.
+__device__ __forceinline__ float lane_value(float v, int u) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), u));
+}
+
 // Weighted sum of one batch of chunk results into (acc0, acc1, wsum) with
-// weights 2^(l - mx); empty chunks (l = -inf) weigh 0 and their (unwritten)
-// results are dropped by the selects.
+// weights 2^(l - mx): the lse of item u is in lane first + u of lv (one
+// load per batch instead of one per chunk), its 8 features of this lane in
+// v[u].  Empty chunks (l = -inf) weigh 0 and their (unwritten) results are
+// dropped by the selects.
 template <int kN>
-__device__ __forceinline__ void accumulate(const float* l, const uint4* v, float mx, f32x4& acc0,
+__device__ __forceinline__ void accumulate(float lv, int first, const uint4* v, float mx, f32x4& acc0,
                                            f32x4& acc1, float& wsum) {
 #pragma unroll
   for (int u = 0; u < kN; ++u) {
-    const float w = l[u] == -INFINITY ? 0.f : exp2f(l[u] - mx);
+    const float l = lane_value(lv, first + u);
+    const float w = l == -INFINITY ? 0.f : exp2f(l - mx);
     const bool use = w != 0.f;
     const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
@@ -158,36 +166,45 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
 
   // ---- first batch of chunk loads, ahead of the weight rows (loads
   //      complete in order, so the merge need not wait for the weights) ----
-  // few chunks: 16 (row, chunk) loads per batch; many: kBatch chunks of a row
+  // few chunks: 16 (row, chunk) items per batch; many: kBatch chunks of a
+  // row.  Item u's lse is loaded by lane u (one load for the batch), its
+  // result by every lane (8 features each).
   constexpr int kItems = kSlots > 0 ? kMergeBatch : kBatch;
+  constexpr int kS = kSlots > 0 ? kSlots : 1;
   constexpr int kRowsPerBatch = kSlots > 0 ? kMergeBatch / kSlots : 1;
-  float l_first[kItems];
+  float l_first;
   uint4 v_first[kItems];
-  auto load_rows = [&](int row0, float* l, uint4* v) {  // kSlots > 0: rows row0 .. + kRowsPerBatch - 1
-#pragma unroll
-    for (int u = 0; u < kItems; ++u) {
-      const int rr = row0 + u / (kSlots > 0 ? kSlots : 1), s = u % (kSlots > 0 ? kSlots : 1);
-      if (rr < nr && s < rm.count(rr)) {  // uniform per wave
-        l[u] = lse_at(rr, s);
-        v[u] = res_at(rr, s);
-      } else {
-        l[u] = -INFINITY;
-        v[u] = make_uint4(0, 0, 0, 0);
+  auto load_rows = [&](int row0, float& lv, uint4* v) {  // kSlots > 0: rows row0 .. + kRowsPerBatch - 1
+    {
+      const int rr = row0 + lane / kS, s = lane % kS;
+      lv = -INFINITY;
+      if (lane < kItems && rr < nr) {
+        if (s < rm.count(rr)) lv = lse_at(rr, s);
       }
     }
+#pragma unroll
+    for (int u = 0; u < kItems; ++u) {
+      const int rr = row0 + u / kS, s = u % kS;
+      if (rr < nr && s < rm.count(rr))  // uniform per wave
+        v[u] = res_at(rr, s);
+      else
+        v[u] = make_uint4(0, 0, 0, 0);
+    }
   };
-  auto load_chunks = [&](int rr, int s0, float* l, uint4* v) {  // kSlots == 0: chunks s0, s0 + 4, ...
+  auto load_chunks = [&](int rr, int s0, float& lv, uint4* v) {  // kSlots == 0: chunks s0, s0 + 4, ...
     const int n = rm.count(rr);
+    {
+      const int s = s0 + kWaves * lane;
+      lv = -INFINITY;
+      if (lane < kBatch && s < n) lv = lse_at(rr, s);
+    }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int s = s0 + kWaves * u;
-      if (s < n) {  // uniform per wave
-        l[u] = lse_at(rr, s);
+      if (s < n)  // uniform per wave
         v[u] = res_at(rr, s);
-      } else {
-        l[u] = -INFINITY;
+      else
         v[u] = make_uint4(0, 0, 0, 0);
-      }
     }
   };
   if (kSlots > 0)
@@ -202,19 +219,16 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
   // the path of a fresh batch, the compiler would wait for every load in
   // flight (the weight rows included) before either.
   if (kSlots > 0) {
-    constexpr int kS = kSlots > 0 ? kSlots : 1;
-    auto merge_rows = [&](int row0, const float* l, const uint4* v) {
+    auto merge_rows = [&](int row0, float lv, const uint4* v) {
 #pragma unroll
       for (int ri = 0; ri < kRowsPerBatch; ++ri) {
         const int rr = row0 + ri;
-        const float* lr = l + ri * kS;
-        const uint4* vr = v + ri * kS;
-        float mx = lr[0];  // the same in every lane (one head)
+        float mx = lane_value(lv, ri * kS);
 #pragma unroll
-        for (int s = 1; s < kS; ++s) mx = fmaxf(mx, lr[s]);
+        for (int s = 1; s < kS; ++s) mx = fmaxf(mx, lane_value(lv, ri * kS + s));
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
         float wsum = 0.f;
-        accumulate<kS>(lr, vr, mx, acc0, acc1, wsum);
+        accumulate<kS>(lv, ri * kS, v + ri * kS, mx, acc0, acc1, wsum);
         if (rr < nr) sh.cb[rr][cb_chunk(rr, lane)] = pack_row(acc0, acc1, wsum);
       }
     };
@@ -222,10 +236,10 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
     if (row0 < nr) {
       merge_rows(row0, l_first, v_first);
       for (row0 += kWaves * kRowsPerBatch; row0 < nr; row0 += kWaves * kRowsPerBatch) {
-        float l[kItems];
+        float lv;
         uint4 v[kItems];
-        load_rows(row0, l, v);
-        merge_rows(row0, l, v);
+        load_rows(row0, lv, v);
+        merge_rows(row0, lv, v);
       }
     }
     __syncthreads();  // every c_bar row written
@@ -236,10 +250,10 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
     auto merge_row = [&](int rr, bool prefetched) {
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       float wsum = 0.f, mx = -INFINITY;
-      auto merge_chunks = [&](const float* l, const uint4* v) {
-        float bmx = l[0];
+      auto merge_chunks = [&](float lv, const uint4* v) {
+        float bmx = lane_value(lv, 0);
 #pragma unroll
-        for (int u = 1; u < kBatch; ++u) bmx = fmaxf(bmx, l[u]);
+        for (int u = 1; u < kBatch; ++u) bmx = fmaxf(bmx, lane_value(lv, u));
         if (bmx > mx) {  // raise the reference of what is summed so far
           const float f = mx == -INFINITY ? 0.f : exp2f(mx - bmx);
           acc0 *= f;
@@ -247,21 +261,21 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
           wsum *= f;
           mx = bmx;
         }
-        accumulate<kBatch>(l, v, mx, acc0, acc1, wsum);
+        accumulate<kBatch>(lv, 0, v, mx, acc0, acc1, wsum);
       };
       if (prefetched) {
         merge_chunks(l_first, v_first);
       } else {
-        float l[kBatch];
+        float lv;
         uint4 v[kBatch];
-        load_chunks(rr, wave, l, v);
-        merge_chunks(l, v);
+        load_chunks(rr, wave, lv, v);
+        merge_chunks(lv, v);
       }
       for (int s0 = wave + kWaves * kBatch; s0 < rm.count(rr); s0 += kWaves * kBatch) {
-        float l[kBatch];
+        float lv;
         uint4 v[kBatch];
-        load_chunks(rr, s0, l, v);
-        merge_chunks(l, v);
+        load_chunks(rr, s0, lv, v);
+        merge_chunks(lv, v);
       }
       if (wave > 0) {
         sh.part_acc[wave - 1][lane][0] = acc0;

@@ -41,6 +41,7 @@ struct Lens {
 };
 
 __device__ __forceinline__ int wave_sum(int v);
+__device__ __forceinline__ int wave_max(int v);
 
 template <typename Fn>
 __device__ __forceinline__ int Lens::sum(Fn fn, int lane) const {
@@ -49,21 +50,58 @@ __device__ __forceinline__ int Lens::sum(Fn fn, int lane) const {
   return wave_sum(acc);
 }
 
+// Cross-lane steps on the VALU (DPP and the gfx950 permlane swaps), not
+// through LDS: a plan is a chain of a few dozen of them.
+//   dpp_perm: lane l receives v from the lane that the DPP control selects
+//   (all sources valid for the controls used here).
+template <int kCtrl>
+__device__ __forceinline__ int dpp_perm(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, false);
+}
+//   dpp_shift: the same with lanes whose source is outside the row (or
+//   whose row the mask leaves out) receiving 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_shift(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xF, false);
+}
+
+// op over the 64 lanes, in every lane: lane pairs l ^ 1, l ^ 2 (quad
+// permutations), the two quads of each 8 (row half mirror), the two 8s of
+// each row of 16 (row mirror), then rows l ^ 16 and l ^ 32 (permlane swaps).
+template <typename Op>
+__device__ __forceinline__ int wave_reduce(int v, Op op) {
+  v = op(v, dpp_perm<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp_perm<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  v = op(v, dpp_perm<0x141>(v));  // row_half_mirror
+  v = op(v, dpp_perm<0x140>(v));  // row_mirror
+  auto a = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+  v = op((int)a[0], (int)a[1]);
+  auto c = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+  return op((int)c[0], (int)c[1]);
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return wave_reduce(v, [](int x, int y) { return x + y; });
+}
+__device__ __forceinline__ int wave_max(int v) {
+  return wave_reduce(v, [](int x, int y) { return x > y ? x : y; });
+}
+
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 within each
+// row of 16, then the last lane of row 0 (2) into row 1 (3), and lane 31
+// into rows 2 and 3.
+__device__ __forceinline__ int wave_scan(int v) {
+  v += dpp_shift<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_shift<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_shift<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_shift<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_shift<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_shift<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
-  return v;
-}
+// Value of v in lane `src` (uniform), in every lane.
+__device__ __forceinline__ int lane_int(int v, int src) { return __builtin_amdgcn_readlane(v, src); }
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
@@ -104,16 +142,16 @@ __device__ __forceinline__ void locate(const Lens& L, int c, int g, int lane, in
   for (int b0 = 0; b0 < L.batch; b0 += 64) {
     const int b = b0 + lane;
     const int n = b < L.batch ? ceil_div(b0 == 0 ? L.mine : seq_len(L.lens, b, L.max_len), c) : 0;
-    const int incl = wave_scan(n, lane);
+    const int incl = wave_scan(n);
     const int start = first + incl - n;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(b < L.batch && g >= start && g < start + n);
     if (hit != 0) {
       const int src = __builtin_ctzll(hit);
       b_out = b0 + src;
-      j_out = g - __shfl(start, src, 64);
+      j_out = g - lane_int(start, src);
       return;
     }
-    first += __shfl(incl, 63, 64);
+    first += lane_int(incl, 63);
   }
 }
 

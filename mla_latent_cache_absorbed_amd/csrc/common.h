@@ -79,9 +79,6 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
 }
 
 // Wave-wide reductions over lanes that differ in the given xor bit(s).
-__device__ __forceinline__ float xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
-}
 __device__ __forceinline__ float xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }

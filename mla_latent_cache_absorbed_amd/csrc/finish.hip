@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
       for (int b0 = 0; b0 < f.batch; b0 += 64) {
         const int b = b0 + lane;
         const int n = b < f.batch ? chunks::ceil_div(b0 == 0 ? lens.mine : chunks::seq_len(f.context_lens, b, f.max_len), c) : 0;
-        const int incl = chunks::wave_scan(n, lane);
+        const int incl = chunks::wave_scan(n);
         const int start = first + incl - n;
         const int src = my_b - b0;
         const int s_start = __shfl(start, src & 63, 64), s_n = __shfl(n, src & 63, 64);
@@ -380,11 +380,9 @@ __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
           my_first = s_start;
           my_count = s_n;
         }
-        first += __shfl(incl, 63, 64);
+        first += chunks::lane_int(incl, 63);
       }
-      int mx = lane < nr ? my_count : 0;
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) mx = max(mx, __shfl_xor(mx, m, 64));
+      const int mx = chunks::wave_max(lane < nr ? my_count : 0);
       if (lane < nr) {
         sh.row_first[lane] = my_first;
         sh.row_count[lane] = my_count;

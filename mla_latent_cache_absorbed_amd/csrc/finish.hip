@@ -44,7 +44,7 @@ constexpr int kDh = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowBlock = 16;  // query rows per work-group (the MFMA N)
-constexpr int kMergeBatch = 16;  // chunk loads in flight per lane
+constexpr int kMaxItems = 32;  // chunk results in flight per lane, at most
 
 // Physical 16-byte chunk of logical chunk c in c_bar row `row` (< 16): the
 // XOR spreads the B-operand reads (16 rows, one chunk each) over the banks.
@@ -166,12 +166,15 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
 
   // ---- first batch of chunk loads, ahead of the weight rows (loads
   //      complete in order, so the merge need not wait for the weights) ----
-  // few chunks: 16 (row, chunk) items per batch; many: kBatch chunks of a
-  // row.  Item u's lse is loaded by lane u (one load for the batch), its
+  // few chunks: each wave merges whole rows, its 4 of the block's 16 in one
+  // batch of (row, chunk) items (up to 8 chunk slots: at most 32 items), or
+  // 2 rows per batch with 16 slots; many chunks: kBatch chunks of a row per
+  // batch.  Item u's lse is loaded by lane u (one load for the batch), its
   // result by every lane (8 features each).
-  constexpr int kItems = kSlots > 0 ? kMergeBatch : kBatch;
+  constexpr int kRowsPerBatch = kSlots > 0 ? (kSlots <= 8 ? kRowBlock / kWaves : kMaxItems / kSlots) : 1;
   constexpr int kS = kSlots > 0 ? kSlots : 1;
-  constexpr int kRowsPerBatch = kSlots > 0 ? kMergeBatch / kSlots : 1;
+  constexpr int kItems = kSlots > 0 ? kRowsPerBatch * kSlots : kBatch;
+  static_assert(kItems <= kMaxItems, "one batch's results fit the registers");
   float l_first;
   uint4 v_first[kItems];
   auto load_rows = [&](int row0, float& lv, uint4* v) {  // kSlots > 0: rows row0 .. + kRowsPerBatch - 1

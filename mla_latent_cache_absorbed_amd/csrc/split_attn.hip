@@ -16,18 +16,20 @@
 // d_c + d_r cached values ("MLA, dim by dim", FLOPs of section 5.2).
 //
 // gfx950 design
-// - 512 threads = 8 wave64s, two per SIMD, in two roles:
+// - 768 threads = 12 wave64s, three per SIMD, in two roles:
 //     score waves 0-3 (one 16-head block each): scores of tile k on
 //       16x16x32 bf16 MFMA, the online softmax, and the bf16 probabilities
 //       P(k) published to LDS (plus per-head rescale factors when the
 //       reference moves);
-//     accumulate waves 4-7 (128 latent features each, all 64 heads): issue
+//     accumulate waves 4-11 (64 latent features each, all 64 heads): issue
 //       the tile DMAs and fold P(k-1) into the fp32 latent accumulator
 //       against tile k-1; every latent operand they read feeds four MFMAs,
 //       one per head block.
-//   Each SIMD runs one wave of each role, so one role's LDS latency is
-//   covered by the other's MFMAs, and each role fits in 256 registers.  One
-//   work-group barrier per tile orders everything.
+//   Each SIMD runs one score wave and two accumulate waves, so one wave's
+//   LDS and DMA latency is covered by the others' MFMAs, and every wave fits
+//   in 168 registers (with two waves per SIMD, 128 features per accumulate
+//   wave, the loop ran 3-7 % slower at T = 32K..128K).  One work-group
+//   barrier per tile orders everything.
 // - The chunk streams in 32-token tiles through a ring of four LDS stages
 //   filled by direct global->LDS DMA (global_load_lds_dwordx4): no staging
 //   registers; tiles k+1 and k+2 are in flight while the score waves read
@@ -81,17 +83,19 @@ constexpr int kDr = 64;
 constexpr int kDkv = kDc + kDr;
 constexpr int kTile = kFastTile;                  // 32 tokens
 constexpr int kBlocks = kFastHeadsPerGroup / 16;  // 16-head blocks per group (4)
-constexpr int kWaves = 8;
+constexpr int kWaves = 12;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kAccWaves = 4;
+constexpr int kAccWaves = 8;
 constexpr int kAccFeatureBlocks = kDc / 16 / kAccWaves;  // 16-feature blocks per accumulate wave
 constexpr int kStages = 4;                        // LDS ring depth
 constexpr int kLatBytes = kTile * kDc * 2;        // 32 KB: 32 rows of 1 KB
 constexpr int kRopeBytes = kTile * kDr * 2;       // 4 KB: 32 rows of 128 B
 constexpr int kStageBytes = kLatBytes + kRopeBytes;
-// Tile DMAs per accumulate wave: 8 latent rows and one block of 8 RoPE rows.
-constexpr int kLatRowsPerWave = kTile / kAccWaves;  // 8
-constexpr int kAccDmas = kLatRowsPerWave + 1;       // 9
+// Tile DMAs per accumulate wave: 4 latent rows (one DMA each) and 4 RoPE
+// rows (one DMA with half the lanes).
+constexpr int kLatRowsPerWave = kTile / kAccWaves;   // 4
+constexpr int kRopeRowsPerWave = kTile / kAccWaves;  // 4
+constexpr int kAccDmas = kLatRowsPerWave + 1;        // 5
 // LDS operand reads kept in flight, in pairs (lgkmcnt counts at most 15)
 constexpr int kScoreReadsAhead = 6;
 constexpr int kAccReadsAhead = 6;
@@ -251,8 +255,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   auto store_result = [&]() {
     uint16_t* po = p.part_o + res_row * kDc;
 #pragma unroll
-    for (int k2 = 0; k2 < kFastHeadsPerGroup / kWaves; ++k2) {
-      const int head = (kFastHeadsPerGroup / kWaves) * wave + k2;
+    for (int k2 = 0; k2 < (kFastHeadsPerGroup + kWaves - 1) / kWaves; ++k2) {
+      const int head = wave + kWaves * k2;
+      if (head >= kFastHeadsPerGroup) break;
       // features 8 lane .. 8 lane + 7: one chunk, its halves swapped for
       // head bit 3
       const u32x4 c = *reinterpret_cast<const AS3 u32x4*>((AS3 uint8_t*)sh.ring + head * (kDc * 2) +
@@ -266,18 +271,18 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   };
 
   // Tile i -> stage i % kStages.  Accumulate wave a copies latent rows
-  // 8a..8a+7 of each tile (one 1 KB row per DMA) and RoPE rows 8a..8a+7 (one
-  // DMA); row0 is the pool row of the tile's first token.  Rows past the end
+  // 4a..4a+3 of each tile (one 1 KB row per DMA) and RoPE rows 4a..4a+3 (one
+  // DMA, lanes 0-31); row0 is the pool row of the tile's first token.  Rows past the end
   // of the chunk repeat the tile's first row, so the LDS never holds
   // non-finite garbage; their probabilities are exactly 0.  All address
   // arithmetic is scalar except the lane offsets.
   const uint32_t ring_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)sh.ring);
-  const int dma_wave = wave & 3;  // accumulate wave index
-  const int rope_row = 8 * dma_wave + (lane >> 3);
+  const int dma_wave = wave - (kWaves - kAccWaves);  // accumulate wave index
+  const int rope_row = kRopeRowsPerWave * dma_wave + ((lane >> 3) & (kRopeRowsPerWave - 1));
   const uint32_t rope_chunk = 16u * (uint32_t)((lane & 7) ^ rope_swz(rope_row));
   const uint32_t rope_voff = (uint32_t)rope_row * (kDr * 2) + rope_chunk;
-  // DMA number `part` of this wave for tile i (parts 0-7: latent rows,
-  // part 8: the RoPE block); t1 ends the chunk.
+  // DMA number `part` of this wave for tile i (parts 0-3: latent rows,
+  // part 4: the RoPE rows); t1 ends the chunk.
   auto dma = [&](int i, int row0, int t1, int part, const uint32_t* lat_voff) {
     const int nvalid = min(kTile, t1 - (t0 + i * kTile));
     const uint32_t sb = ring_base + (uint32_t)((i % kStages) * kStageBytes);
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
     } else {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(p.rope_pool) + (size_t)row0 * (kDr * 2);
       const uint32_t voff = rope_row < nvalid ? rope_voff : rope_chunk;
-      lds_dma16(src, voff, sb + kLatBytes + 8 * dma_wave * (kDr * 2));
+      if (lane < 8 * kRopeRowsPerWave) lds_dma16(src, voff, sb + kLatBytes + kRopeRowsPerWave * dma_wave * (kDr * 2));
     }
   };
 
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   }
   // tile 0 has landed (tile 1 may still be in flight: the loop waits for
   // it before barrier 1)
-  if (ntiles > 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  if (ntiles > 1) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();  // tile_row is visible, tile 0 is in LDS
 
@@ -513,9 +518,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
 
   for (int it = 0; it <= ntiles; ++it) {
     if (it < ntiles) {  // this wave's DMAs of tile it have landed
-      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      if (it + 1 < ntiles) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      static_assert(kAccDmas == 9, "the vmcnt above counts one tile of an accumulate wave's DMAs");
+      static_assert(kAccDmas == 5, "the vmcnt above counts one tile of an accumulate wave's DMAs");
     }
     block_barrier();
     const bool more = it + 2 < ntiles;  // tile it + 2 goes out during this iteration

@@ -265,6 +265,106 @@ def test_repeat_runs_are_bitwise_identical(torch):
     assert torch.equal(first, dw.out)
 
 
+# --------------------------------------------------------------------------
+# score structure: the online softmax's reference maximum moves mid-chunk
+# --------------------------------------------------------------------------
+def _spike_scores(wl, levels, period, q_r_value=8.0):
+    """Rewrite q_R and the RoPE cache so that every head's RoPE logit is 0
+    except at offsets o of each `period`-token window, where it is
+    levels[o] (in natural-log units); the content logits stay random (unit
+    scale).  Every query row and head gets q_R = q_r_value * e_0, and token
+    t's RoPE row gets levels[t % period] / (q_r_value * scale) in its
+    component 0 (then rounded to the storage type, which the oracle reads
+    too)."""
+    f32 = np.float32
+    q_r = np.zeros((wl.batch, wl.n_q, wl.h, wl.d_r), dtype=f32)
+    q_r[..., 0] = q_r_value
+    rope = inputs.as_f32(wl, "rope_pool").copy()
+    rope[..., 0] = 0.0
+    for b in range(wl.batch):
+        for t in range(int(wl.lens[b])):
+            lvl = levels.get(t % period)
+            if lvl is not None:
+                page = wl.page_table[b, t // wl.page_size]
+                rope[page, t % wl.page_size, 0] = lvl / (q_r_value * wl.scale)
+    to_store = inputs.bf16_bits if wl.dtype == "bf16" else (lambda x: x)
+    wl.arrays["q_r"] = to_store(q_r)
+    wl.arrays["rope_pool"] = to_store(rope)
+    return wl
+
+
+# Rising spikes 10, 20 and 30 natural-log units above the random logits, at
+# offsets 40, 80 and 120 of every 128 tokens: each is more than 2^8 above
+# the previous maximum, so every chunk that holds a window moves its
+# reference maximum three times, across tile boundaries, and what was
+# accumulated before each move must be rescaled (a missing or wrong rescale
+# weighs it e^10 times too much or too little).
+_RISING = {40: 10.0, 80: 20.0, 120: 30.0}
+
+
+@pytest.mark.parametrize("splits", [0, 1, 7])
+def test_rising_scores_rescale_the_accumulator(torch, splits):
+    wl = _spike_scores(inputs.make("ds2_t4k", seed=240), _RISING, 128)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "rising spikes S=%d" % splits)
+
+
+def test_rising_scores_paged_ragged_batch(torch):
+    """Planned chunking over a shuffled page table, lengths that end inside
+    a window (some before a spike, some between two)."""
+    wl = inputs.make("ds2_paged_b32", batch=5, lens=("list", [3000, 100, 77, 1150, 41]), seed=241)
+    _spike_scores(wl, _RISING, 128)
+    dw = _run(wl, torch)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "rising spikes, paged")
+
+
+def test_rising_scores_multi_token(torch):
+    """Four causal query tokens; in the second sequence the visible ranges of
+    query rows 0 and 1 end on either side of a spike."""
+    wl = inputs.make("ds2_mtp_b16", batch=2, lens=("list", [1000, 2178]), seed=242)
+    _spike_scores(wl, {40: 10.0, 80: 20.0, 120: 30.0, 127: 40.0}, 128)
+    dw = _run(wl, torch, num_splits=0)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "rising spikes, n_q=4")
+
+
+@pytest.mark.parametrize("splits", [0, 1])
+def test_falling_scores_keep_the_first_reference(torch, splits):
+    """The highest logits first (40 units above the rest at offset 0 of
+    every 128-token window, 30 at offset 1): chunks start on a window, so
+    each sets its reference in its first tile and never moves it, and most
+    weights are tiny (e^-30 .. e^-40) but not zero."""
+    wl = _spike_scores(inputs.make("ds2_t4k", seed=243), {0: 40.0, 1: 30.0}, 128)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16", "falling spikes S=%d" % splits)
+
+
+@pytest.mark.parametrize("splits", [0, 2])
+def test_rising_scores_general_path(torch, splits):
+    """The fp32 general path's online softmax under the same spikes."""
+    wl = _spike_scores(inputs.make("tiny_fp32", lens=("fixed", 300), seed=244), _RISING, 128)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_explicit(problem(wl)), "f32", "general fp32, rising spikes")
+
+
+def test_zero_query_averages_the_latents(torch):
+    """q = 0 and q_R = 0: every visible token weighs the same, so o_i =
+    W_UV[i] (mean of the latents), a closed form independent of the oracle's
+    softmax."""
+    wl = inputs.make("ds2_t4k", batch=2, lens=("list", [1000, 333]), shuffled=True, seed=245)
+    wl.arrays["q"] = np.zeros_like(wl.arrays["q"])
+    wl.arrays["q_r"] = np.zeros_like(wl.arrays["q_r"])
+    dw = _run(wl, torch, out_dtype="f32")
+    lat = inputs.as_f64(wl, "latent_pool")
+    w_uv = inputs.as_f64(wl, "w_uv")
+    ref = np.empty((wl.batch, wl.n_q, wl.h, wl.d_h))
+    for b in range(wl.batch):
+        L = int(wl.lens[b])
+        rows = [lat[wl.page_table[b, t // wl.page_size], t % wl.page_size] for t in range(L)]
+        mean = np.mean(rows, axis=0)
+        ref[b, 0] = w_uv @ mean
+    check(dw.result_f64(), ref, "bf16", "zero query")
+
+
 def test_general_path_bf16_odd_shapes(torch):
     """bf16 storage with shapes outside the MFMA kernels (general path)."""
     wl = inputs.make("tiny_fp32", dtype="bf16", h=6, d_c=40, d_r=6, d_h=12, page_size=8,

@@ -158,10 +158,25 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
                                             int a_base, int rb, int nr, int wave, int lane, bf16x8* wa) {
   const int h = f.h;
   const int g = lane >> 4, l16 = lane & 15;
-  // lse and this lane's 8 features of chunk s of row rb + rr (s < count(rr))
-  auto lse_at = [&](int rr, int s) { return f.part_lse[rm.base(rr) + (size_t)s * rm.step()]; };
-  auto res_at = [&](int rr, int s) {
-    return *reinterpret_cast<const uint4*>(f.part_o + (rm.base(rr) + (size_t)s * rm.step()) * kDc + 8 * lane);
+  // lse index of chunk 0 of row rb + l, in lane l < nr: each row's base is
+  // worked out once, by its own lane (its division by n_q, repeated per
+  // load, had delayed the loads' issue).  It fits an int: the chunk
+  // results it indexes take 1 KB each.
+  const int lane_base = lane < nr ? static_cast<int>(rm.base(lane)) : 0;
+  auto base_of = [&](int rr) { return __builtin_amdgcn_readlane(lane_base, rr); };  // rr wave-uniform
+  // lse of chunk s of row rb + rr (s < count(rr)); a row's chunk results
+  // are `res_step` elements apart, from this lane's 8 features of chunk 0
+  // at row_res(rr)
+  const size_t lse_step = rm.step();
+  const size_t res_step = lse_step * kDc;
+  auto row_res = [&](int rr) { return f.part_o + (size_t)base_of(rr) * kDc + 8 * lane; };
+  // An item past its row's chunks weighs 0 (its lse is -inf) and its value
+  // is dropped by the merge's selects: it loads from a fixed valid address
+  // (the first kilobyte of W_UV) instead of branching around the load, so
+  // that no zero-fill joins a loaded register and forces a wait.
+  const uint16_t* dummy = f.w_uv + 8 * lane;
+  auto res_at = [&](const uint16_t* row, int s, bool valid) {
+    return *reinterpret_cast<const uint4*>(valid ? row + (size_t)s * res_step : dummy);
   };
 
   // ---- first batch of chunk loads, ahead of the weight rows (loads
@@ -180,18 +195,24 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
   auto load_rows = [&](int row0, float& lv, uint4* v) {  // kSlots > 0: rows row0 .. + kRowsPerBatch - 1
     {
       const int rr = row0 + lane / kS, s = lane % kS;
+      const int base = __shfl(lane_base, rr < nr ? rr : 0, 64);
       lv = -INFINITY;
       if (lane < kItems && rr < nr) {
-        if (s < rm.count(rr)) lv = lse_at(rr, s);
+        if (s < rm.count(rr)) lv = f.part_lse[(size_t)base + (size_t)s * lse_step];
       }
+    }
+    const uint16_t* row[kRowsPerBatch];
+    int cnt[kRowsPerBatch];
+#pragma unroll
+    for (int ri = 0; ri < kRowsPerBatch; ++ri) {
+      const int rr = row0 + ri;
+      cnt[ri] = rr < nr ? rm.count(rr) : 0;
+      row[ri] = rr < nr ? row_res(rr) : f.part_o;
     }
 #pragma unroll
     for (int u = 0; u < kItems; ++u) {
-      const int rr = row0 + u / kS, s = u % kS;
-      if (rr < nr && s < rm.count(rr))  // uniform per wave
-        v[u] = res_at(rr, s);
-      else
-        v[u] = make_uint4(0, 0, 0, 0);
+      const int ri = u / kS, s = u % kS;
+      v[u] = res_at(row[ri], s, s < cnt[ri]);
     }
   };
   auto load_chunks = [&](int rr, int s0, float& lv, uint4* v) {  // kSlots == 0: chunks s0, s0 + 4, ...
@@ -199,15 +220,13 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
     {
       const int s = s0 + kWaves * lane;
       lv = -INFINITY;
-      if (lane < kBatch && s < n) lv = lse_at(rr, s);
+      if (lane < kBatch && s < n) lv = f.part_lse[(size_t)base_of(rr) + (size_t)s * lse_step];
     }
+    const uint16_t* row = row_res(rr);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int s = s0 + kWaves * u;
-      if (s < n)  // uniform per wave
-        v[u] = res_at(rr, s);
-      else
-        v[u] = make_uint4(0, 0, 0, 0);
+      v[u] = res_at(row, s, s < n);
     }
   };
   if (kSlots > 0)
@@ -344,6 +363,11 @@ template <bool kBf16Out, int kSlots, int kBatch>
 __global__ __launch_bounds__(kThreads) void finish_bf16_kernel(FinishArgs f) {
   __shared__ __attribute__((aligned(16))) MergeShared sh;
 
+  // every kernel argument in registers before the first branch (else the
+  // pointers come in a second scalar load after it, one more memory
+  // latency before the first loads issue)
+  asm volatile("" ::"s"(f.part_o), "s"(f.part_lse), "s"(f.w_uv), "s"(f.out), "s"(f.context_lens), "s"(f.max_len),
+               "s"(f.slots), "s"(f.plan_target), "s"(f.plan_min), "s"(f.plan_max));
   // blockIdx.x = head + h * (W_UV half + 2 * row block): congruent mod 8
   // for one head when h % 8 == 0
   const int head = blockIdx.x % f.h;

@@ -197,6 +197,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   const int lane = tid & 63;
   const int g = lane >> 4, l16 = lane & 15;
 
+  // every kernel argument in registers before the first branch (else the
+  // pointers, in another 64-byte line of the argument block, come in a
+  // second scalar load after it: one more memory latency)
+  asm volatile("" ::"s"(p.q_abs), "s"(p.q_r), "s"(p.latent_pool), "s"(p.rope_pool), "s"(p.page_table),
+               "s"(p.context_lens), "s"(p.part_o), "s"(p.part_lse));
   // ---- which (global chunk, query token, head group) this group owns ----
   const int sharers = p.n_q * p.head_groups;
   const int x = blockIdx.x;

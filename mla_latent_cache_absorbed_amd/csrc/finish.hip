@@ -90,6 +90,10 @@ struct RowMap {
   __device__ __forceinline__ int count(int rr) const { return kPlanned ? count_[rr] : slots; }
 };
 
+// 2^x on the hardware exp2 (one instruction; a result below 2^-126 flushes
+// to 0, a weight far too small to matter next to the largest, which is 1).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Value of v in lane u (u uniform), as a scalar.
 __device__ __forceinline__ float lane_value(float v, int u) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), u));
@@ -106,7 +110,7 @@ __device__ __forceinline__ void accumulate(float lv, int first, const uint4* v, 
 #pragma unroll
   for (int u = 0; u < kN; ++u) {
     const float l = lane_value(lv, first + u);
-    const float w = l == -INFINITY ? 0.f : exp2f(l - mx);
+    const float w = l == -INFINITY ? 0.f : exp2_hw(l - mx);
     const bool use = w != 0.f;
     const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
@@ -165,18 +169,28 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
   const int lane_base = lane < nr ? static_cast<int>(rm.base(lane)) : 0;
   auto base_of = [&](int rr) { return __builtin_amdgcn_readlane(lane_base, rr); };  // rr wave-uniform
   // lse of chunk s of row rb + rr (s < count(rr)); a row's chunk results
-  // are `res_step` elements apart, from this lane's 8 features of chunk 0
-  // at row_res(rr)
+  // are `res_step` elements apart from chunk 0 at row_res(rr) (a
+  // wave-uniform address; each lane adds its 16-byte offset as a 32-bit
+  // vector offset, so that every load is a scalar base plus a vector offset
+  // and no 64-bit address is kept per load)
   const size_t lse_step = rm.step();
   const size_t res_step = lse_step * kDc;
-  auto row_res = [&](int rr) { return f.part_o + (size_t)base_of(rr) * kDc + 8 * lane; };
+  const uint32_t lane_off = 16u * (uint32_t)lane;
   // An item past its row's chunks weighs 0 (its lse is -inf) and its value
-  // is dropped by the merge's selects: it loads from a fixed valid address
-  // (the first kilobyte of W_UV) instead of branching around the load, so
-  // that no zero-fill joins a loaded register and forces a wait.
-  const uint16_t* dummy = f.w_uv + 8 * lane;
-  auto res_at = [&](const uint16_t* row, int s, bool valid) {
-    return *reinterpret_cast<const uint4*>(valid ? row + (size_t)s * res_step : dummy);
+  // is dropped by the merge's selects: it loads the row's last chunk again
+  // (a row without chunks: the first kilobyte of W_UV) instead of branching
+  // around the load, so that no zero-fill joins a loaded register and
+  // forces a wait.
+  struct RowRes {
+    const uint8_t* first;  // chunk 0 of the row (wave-uniform)
+    int last;              // its last chunk, clamped to 0
+  };
+  auto row_res = [&](int rr, int n) {
+    return n > 0 ? RowRes{reinterpret_cast<const uint8_t*>(f.part_o + (size_t)base_of(rr) * kDc), n - 1}
+                 : RowRes{reinterpret_cast<const uint8_t*>(f.w_uv), 0};
+  };
+  auto res_at = [&](const RowRes& row, int s) {
+    return *reinterpret_cast<const uint4*>(row.first + (size_t)min(s, row.last) * (res_step * 2) + lane_off);
   };
 
   // ---- first batch of chunk loads, ahead of the weight rows (loads
@@ -201,19 +215,14 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
         if (s < rm.count(rr)) lv = f.part_lse[(size_t)base + (size_t)s * lse_step];
       }
     }
-    const uint16_t* row[kRowsPerBatch];
-    int cnt[kRowsPerBatch];
+    RowRes row[kRowsPerBatch];
 #pragma unroll
     for (int ri = 0; ri < kRowsPerBatch; ++ri) {
       const int rr = row0 + ri;
-      cnt[ri] = rr < nr ? rm.count(rr) : 0;
-      row[ri] = rr < nr ? row_res(rr) : f.part_o;
+      row[ri] = row_res(rr, rr < nr ? rm.count(rr) : 0);
     }
 #pragma unroll
-    for (int u = 0; u < kItems; ++u) {
-      const int ri = u / kS, s = u % kS;
-      v[u] = res_at(row[ri], s, s < cnt[ri]);
-    }
+    for (int u = 0; u < kItems; ++u) v[u] = res_at(row[u / kS], u % kS);
   };
   auto load_chunks = [&](int rr, int s0, float& lv, uint4* v) {  // kSlots == 0: chunks s0, s0 + 4, ...
     const int n = rm.count(rr);
@@ -222,12 +231,9 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
       lv = -INFINITY;
       if (lane < kBatch && s < n) lv = f.part_lse[(size_t)base_of(rr) + (size_t)s * lse_step];
     }
-    const uint16_t* row = row_res(rr);
+    const RowRes row = row_res(rr, n);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int s = s0 + kWaves * u;
-      v[u] = res_at(row, s, s < n);
-    }
+    for (int u = 0; u < kBatch; ++u) v[u] = res_at(row, s0 + kWaves * u);
   };
   if (kSlots > 0)
     load_rows(wave * kRowsPerBatch, l_first, v_first);
@@ -277,7 +283,7 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
 #pragma unroll
         for (int u = 1; u < kBatch; ++u) bmx = fmaxf(bmx, lane_value(lv, u));
         if (bmx > mx) {  // raise the reference of what is summed so far
-          const float f = mx == -INFINITY ? 0.f : exp2f(mx - bmx);
+          const float f = mx == -INFINITY ? 0.f : exp2_hw(mx - bmx);
           acc0 *= f;
           acc1 *= f;
           wsum *= f;
@@ -310,14 +316,14 @@ __device__ __forceinline__ void finish_rows(const FinishArgs& f, MergeShared& sh
         float mall = mx;
 #pragma unroll
         for (int k = 1; k < kWaves; ++k) mall = fmaxf(mall, sh.red[k]);
-        const float f0 = mx == -INFINITY ? 0.f : exp2f(mx - mall);
+        const float f0 = mx == -INFINITY ? 0.f : exp2_hw(mx - mall);
         acc0 *= f0;
         acc1 *= f0;
         wsum *= f0;
 #pragma unroll
         for (int k = 0; k < kWaves - 1; ++k) {
           const float mk = sh.red[k + 1];
-          const float fk = mk == -INFINITY ? 0.f : exp2f(mk - mall);
+          const float fk = mk == -INFINITY ? 0.f : exp2_hw(mk - mall);
           acc0 += fk * sh.part_acc[k][lane][0];
           acc1 += fk * sh.part_acc[k][lane][1];
           wsum += fk * sh.part_w[k][lane];

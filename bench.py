@@ -376,6 +376,10 @@ def main():
                    "chunk_len": chunk, "layers_rotated": n_layers},
         "cache_gbps": c["step"]["cache_bytes"] / step_s / 1e9,
         "roofline": roof,
+        # the whole step against the same HBM peak: the bytes the method must
+        # move per step (cache read once, W_UK and W_UV once) over its wall time
+        "step_hbm": dict(algorithmic_bytes=c["step"]["bytes"], achieved=c["step"]["bytes"] / step_s / 1e9,
+                         peak=HBM_GBPS, unit="GB/s", frac=c["step"]["bytes"] / step_s / 1e9 / HBM_GBPS),
         "kernels": {k: dict(avg_us=kern[k] * 1e6, **rooflines[k]) for k in kern},
     }
 
@@ -391,7 +395,7 @@ def main():
                  roofline=kernel_roofline(k, c2[k], t_split, wl2.dtype))
         if step2 is not None:
             e.update(step_us=step2 * 1e6, step_tflops=c2["step"]["flops"] / step2 / 1e12,
-                     graph_step_us=graph2 * 1e6)
+                     step_hbm_gbps=c2["step"]["bytes"] / step2 / 1e9, graph_step_us=graph2 * 1e6)
         return e
 
     sweep = {}

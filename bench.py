@@ -145,13 +145,37 @@ def layer_bytes(wl):
     return el * (wl.num_pages * wl.page_size * (wl.d_c + wl.d_r) + 2 * wl.h * wl.d_h * wl.d_c)
 
 
+def prepared_calls(dw, layers):
+    """The C entry point and one argument tuple per layer set, marshalled
+    once: every set goes through the checked binding first (shapes, dtypes,
+    device, contiguity), and the timed loop then calls mla_decode_run with
+    the same pointers directly.  The per-call checks in Python take about as
+    long as a whole T=4K step on the GPU, so in the loop they would set the
+    launch rate instead of the kernels."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding
+    stream = torch.cuda.current_stream().cuda_stream
+    wl = dw.wl
+    calls = []
+    for t in layers.sets:
+        dw.run(**t)
+        calls.append((dw.dec.plan, wl.batch, wl.n_q, dw.max_len, int(t["latent_pool"].shape[0]),
+                      t["q"].data_ptr(), t["q_r"].data_ptr(), t["latent_pool"].data_ptr(),
+                      t["rope_pool"].data_ptr(), t["page_table"].data_ptr(), t["context_lens"].data_ptr(),
+                      t["w_uk"].data_ptr(), t["w_uv"].data_ptr(), dw.out.data_ptr(), dw.ws.data_ptr(),
+                      dw.ws.numel() * dw.ws.element_size(), stream))
+    torch.cuda.synchronize()
+    return binding.lib().mla_decode_run, calls
+
+
 def time_steps(dw, layers, steps, warmup, per_kernel):
     """Average step time (s); with per_kernel, also per-kernel averages (s)."""
     import torch
     from mla_latent_cache_absorbed_amd import binding
     n = len(layers)
+    run, calls = prepared_calls(dw, layers)
     for i in range(warmup):
-        dw.run(**layers.sets[i % n])
+        binding.raise_for_status(run(*calls[i % n]))
     torch.cuda.synchronize()
     if per_kernel:
         binding.mla_decode_enable_timing(dw.dec.plan, steps)
@@ -159,9 +183,11 @@ def time_steps(dw, layers, steps, warmup, per_kernel):
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
+    status = 0
     for i in range(steps):
-        dw.run(**layers.sets[(warmup + i) % n])
+        status = min(status, run(*calls[(warmup + i) % n]))  # failures are negative
     end.record()
+    binding.raise_for_status(status)
     torch.cuda.synchronize()
     step_s = start.elapsed_time(end) / 1e3 / steps
     kernels = None

@@ -94,6 +94,12 @@ def _check(status: int) -> int:
     return status
 
 
+def raise_for_status(status: int) -> int:
+    """Raise MLAError (with mla_decode_last_error's text) for a failed status
+    returned by a direct call of the library; returns the status otherwise."""
+    return _check(status)
+
+
 def make_config(h, d_c, d_r, d_h, dtype="bf16", out_dtype=None, page_size=64, max_batch=1,
                 max_q_per_seq=1, max_pages_per_seq=1, num_splits=0, scale=0.0) -> Config:
     code = {"bf16": MLA_DTYPE_BF16, "f32": MLA_DTYPE_F32}

@@ -418,7 +418,8 @@ def main():
                  / t_split / 1e9,
                  tflops=c2["split_attn"]["flops"] / t_split / 1e12,
                  kernels_us={kk: v * 1e6 for kk, v in kern2.items()},
-                 roofline=kernel_roofline(k, c2[k], t_split, wl2.dtype))
+                 roofline=dict(kernel_roofline(k, c2[k], t_split, wl2.dtype),
+                               traffic=measured_traffic(k, wl2.name)))
         if step2 is not None:
             e.update(step_us=step2 * 1e6, step_tflops=c2["step"]["flops"] / step2 / 1e12,
                      step_hbm_gbps=c2["step"]["bytes"] / step2 / 1e9, graph_step_us=graph2 * 1e6)

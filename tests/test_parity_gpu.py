@@ -210,6 +210,19 @@ def test_four_head_groups_two_query_tokens(torch, splits):
           "h=256 n_q=2 S=%d" % splits)
 
 
+@pytest.mark.parametrize("splits", [0, 4])
+def test_three_head_groups_three_query_tokens(torch, splits):
+    """h = 192 (an odd number of 64-head groups, so the work-groups of one
+    chunk do not fill a multiple of eight) and three query tokens per
+    sequence (causal diagonals of three rows, finish row blocks that mix
+    sequences), with planned and fixed chunking."""
+    wl = inputs.make("ds2_mtp_b16", h=192, n_q=3, batch=5, lens=("list", [3, 95, 1200, 41, 600]),
+                     shuffled=True, seed=250)
+    dw = _run(wl, torch, num_splits=splits)
+    check(dw.result_f64(), oracle.decode_absorbed(problem(wl)), "bf16",
+          "h=192 n_q=3 S=%d" % splits)
+
+
 @pytest.mark.parametrize("page_size,splits", [(32, 0), (32, 5), (256, 0), (256, 3)])
 def test_page_sizes(torch, page_size, splits):
     """Pages of one tile (32 tokens) and of eight (256): the fast path's

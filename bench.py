@@ -15,6 +15,9 @@ row for each of the two projections, softmax excluded); `cache_gbps` is the
 latent + RoPE cache bytes per step over the step time.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The headline workload is B=1, T=32K (the split kernel's roofline bar point);
+the other DeepSeek-V2-shaped configurations are measured in `sweep`.
 """
 from __future__ import annotations
 
@@ -201,6 +204,57 @@ def time_steps(dw, layers, steps, warmup, per_kernel):
     return step_s, kernels
 
 
+def stats(values):
+    """mean, median, p10, p90 (nearest-rank) and count of a list of numbers."""
+    v = sorted(values)
+    n = len(v)
+
+    def rank(q):
+        return v[min(n - 1, max(0, int(math.ceil(q * n)) - 1))]
+    return dict(mean=sum(v) / n, median=rank(0.5), p10=rank(0.1), p90=rank(0.9), n=n)
+
+
+def step_distribution(dw, layers, n):
+    """n more steps, each between two events recorded on torch's current
+    stream (the stream the library launches on): per-step seconds."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding
+    run, calls = prepared_calls(dw, layers)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    status = 0
+    ev[0].record()
+    for i in range(n):
+        status = min(status, run(*calls[i % len(calls)]))
+        ev[i + 1].record()
+    binding.raise_for_status(status)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(n)]
+
+
+def kernel_distribution(dw, layers, n):
+    """n more steps with every kernel's own start and stop recorded by its
+    dispatch (events on the kernel's stream): per-run seconds of each kernel."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding
+    run, calls = prepared_calls(dw, layers)
+    binding.mla_decode_enable_timing(dw.dec.plan, n)
+    torch.cuda.synchronize()
+    status = 0
+    for i in range(n):
+        status = min(status, run(*calls[i % len(calls)]))
+    binding.raise_for_status(status)
+    per_run = binding.mla_decode_read_timing_runs(dw.dec.plan, n)
+    binding.mla_decode_enable_timing(dw.dec.plan, 0)
+    out = {}
+    for r in per_run:
+        if r.get("up_project", 0) == 0:  # merge and up-projection ran as one kernel
+            r = {"q_absorb": r["q_absorb"], "split_attn": r["split_attn"], "finish": r["combine"]}
+        for k, v in r.items():
+            out.setdefault(k, []).append(v / 1e3)
+    return out
+
+
 def achievable_peaks():
     """What plain library work reaches on this GPU, for context beside the
     vendor peaks: a 1 GiB device-to-device copy (read + write bytes) and a
@@ -270,61 +324,118 @@ def time_graph(dw, layers, steps, warmup):
     return start.elapsed_time(end) / 1e3 / (reps * n)
 
 
-def cpu_baseline(wl, target_s=15.0):
-    """Time the fp64 oracle (explicit K/V form, as it stands) on a bounded
-    sample of the workload: whole decode of a subset of (sequence, head)
-    pairs, sized for about target_s seconds of CPU work."""
-    import numpy as np
+def measured_counters(kernel, workload):
+    """MFMA utilisation and LDS figures of one kernel from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel
+    source changed since."""
+    from mla_latent_cache_absorbed_amd.profiling import COUNTERS_FILE, source_digest
+    try:
+        with open(COUNTERS_FILE) as f:
+            e = json.load(f)[kernel][workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("source_digest") != source_digest(kernel):
+        return None
+    return e
+
+
+def host_cpu():
+    """CPU model and core counts of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return dict(cpu_model=model, nproc=os.cpu_count(), usable_cpus=usable)
+
+
+def oracle_rate(wl, target_s, threads=None):
+    """TFLOP/s of the explicit fp64 oracle (as it stands) on a bounded sample
+    of whole (sequence, head) pairs of the workload, sized for about target_s
+    seconds; with `threads`, on that many OpenMP threads."""
     import oracle
     from mla_latent_cache_absorbed_amd import inputs
     prob = oracle.Problem(**inputs.oracle_problem_kwargs(wl))
-    threads = oracle.num_threads()
-    all_pairs = [(b, i) for b in range(wl.batch) for i in range(wl.h)]
+    saved = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    try:
+        used = oracle.num_threads()
+        all_pairs = [(b, i) for b in range(wl.batch) for i in range(wl.h)]
 
-    def run(n):
-        pairs = all_pairs[:n]
-        t = time.perf_counter()
-        oracle.decode_explicit(prob, pairs)
-        return time.perf_counter() - t, pairs
+        def run(n):
+            pairs = all_pairs[:n]
+            t = time.perf_counter()
+            oracle.decode_explicit(prob, pairs)
+            return time.perf_counter() - t, pairs
 
-    n = min(len(all_pairs), max(1, threads))
-    dt, pairs = run(n)
-    if dt < target_s / 3:
-        n = int(min(len(all_pairs), max(n, round(n * target_s / max(dt, 1e-3)))))
+        n = min(len(all_pairs), max(1, used))
         dt, pairs = run(n)
-    reps = 1
-    if dt < target_s / 3:  # the whole workload is short: repeat it for a steadier figure
-        reps = max(1, int(round(target_s / max(dt, 1e-3))))
-        t = time.perf_counter()
-        for _ in range(reps):
-            run(n)
-        dt = (time.perf_counter() - t) / reps
+        if dt < target_s / 3:
+            n = int(min(len(all_pairs), max(n, round(n * target_s / max(dt, 1e-3)))))
+            dt, pairs = run(n)
+        reps = 1
+        if dt < target_s / 3:  # the whole workload is short: repeat it for a steadier figure
+            reps = max(1, int(round(target_s / max(dt, 1e-3))))
+            t = time.perf_counter()
+            for _ in range(reps):
+                run(n)
+            dt = (time.perf_counter() - t) / reps
+    finally:
+        oracle.set_num_threads(saved)
     per_pair = 4 * wl.d_c + 2 * wl.d_r + 1
     flops = 0
     for b, _ in pairs:
         L = int(wl.lens[b])
         flops += sum(L - wl.n_q + m + 1 for m in range(wl.n_q)) * per_pair
         flops += wl.n_q * 2 * 2 * wl.d_h * wl.d_c
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=min(threads, len(pairs)),
-                kind="oracle",
+    return dict(value=flops / dt / 1e12, seconds=dt, reps=reps, pairs=len(pairs), of=len(all_pairs),
+                threads=min(used, len(pairs)))
+
+
+def cpu_baseline(wl, target_s=15.0):
+    """The fp64 oracle (explicit K/V form, as it stands) timed on this host:
+    on all its threads for the measured workload, and on one thread for the
+    tiny fp32 and the T=4K configurations."""
+    from mla_latent_cache_absorbed_amd import inputs
+    main = oracle_rate(wl, target_s)
+    one = {}
+    for name in ("tiny_fp32", "ds2_t4k"):
+        r = oracle_rate(inputs.make(name), 5.0, threads=1)
+        one[name] = dict(value=r["value"], unit="TFLOP/s", seconds_per_pass=r["seconds"],
+                         sample="%d of %d (sequence, head) pairs, mean of %d pass(es)"
+                                % (r["pairs"], r["of"], r["reps"]))
+    return dict(value=main["value"], unit="TFLOP/s", cores=main["threads"], kind="oracle",
                 sample="explicit fp64 oracle (per-head K/V rebuilt, textbook softmax) on %d of "
                        "%d (sequence, head) pairs of %s, %.2f s wall per pass, mean of %d pass(es)"
-                       % (len(pairs), len(all_pairs), wl.name, dt, reps),
-                seconds=dt)
+                       % (main["pairs"], main["of"], wl.name, main["seconds"], main["reps"]),
+                seconds=main["seconds"], one_thread=one, **host_cpu())
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ds2_t4k")
-    ap.add_argument("--extra", default="ds2_t32k,ds2_t128k,ds2_paged_b32,ds2_mtp_b16",
-                    help="comma-separated further workloads whose steps and split kernel are "
-                         "also measured ('' = none)")
+    ap.add_argument("--workload", default="ds2_t32k",
+                    help="headline workload (B=1, T=32K: the split kernel's roofline bar point)")
+    ap.add_argument("--extra", default="ds2_t4k,ds2_t128k,ds2_paged_b32,ds2_mtp_b16",
+                    help="comma-separated further workloads whose steps and kernels are also "
+                         "measured ('' = none)")
+    ap.add_argument("--dist-runs", type=int, default=100,
+                    help="runs behind each median / p10 / p90 (at least --steps)")
     ap.add_argument("--no-achievable", action="store_true",
                     help="skip the copy and GEMM measurements of achievable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--layers", type=int, default=0, help="0 = enough for 1 GiB")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run plain device-to-device copies of MB MiB (the reference kernel "
@@ -353,6 +464,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": args.steps}))
         return
 
+    num_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    dist_runs = max(args.dist_runs, args.steps)
+
     def measure(name, steps, warmup):
         wl = inputs.make(name)
         dw = DeviceWorkload(wl)
@@ -362,35 +476,60 @@ def main():
         log("%s: %d layers rotated (%.0f MB each), %d chunks of %d tokens" %
             (name, n_layers, layer_bytes(wl) / 1e6, splits, chunk))
         step_s, _ = time_steps(dw, layers, steps, warmup, per_kernel=False)
-        graph_s = time_graph(dw, layers, steps, warmup)
-        log("%s: step %.2f us eager, %.2f us replayed from a HIP graph" % (name, step_s * 1e6, graph_s * 1e6))
-        _, kern = time_steps(dw, layers, steps, 2, per_kernel=True)
-        c = counts(wl, chunk_count(wl, splits, chunk, torch.cuda.get_device_properties(0).multi_processor_count))
+        graph_s = None if args.no_graph else time_graph(dw, layers, steps, warmup)
+        step_dist = stats(step_distribution(dw, layers, dist_runs))
+        kern_dist = {k: stats(v) for k, v in kernel_distribution(dw, layers, dist_runs).items()}
+        log("%s: step %.2f us (mean of %d); median %.2f us over %d; kernels (median us): %s" %
+            (name, step_s * 1e6, steps, step_dist["median"] * 1e6, dist_runs,
+             {k: round(v["median"] * 1e6, 2) for k, v in kern_dist.items()}))
+        c = counts(wl, chunk_count(wl, splits, chunk, num_cus))
         del layers
-        return wl, dw, c, step_s, graph_s, kern, splits, chunk, n_layers
+        return dict(wl=wl, c=c, step_s=step_s, graph_s=graph_s, step_dist=step_dist, kern=kern_dist,
+                    splits=splits, chunk=chunk, n_layers=n_layers)
 
-    wl, dw, c, step_s, graph_s, kern, splits, chunk, n_layers = measure(args.workload, args.steps,
-                                                                       args.warmup)
-    log("step %.2f us; kernels (us): %s" % (step_s * 1e6, {k: round(v * 1e6, 2) for k, v in kern.items()}))
+    def us(d):
+        return {k: d[k] * 1e6 for k in ("mean", "median", "p10", "p90")}
 
-    rooflines = {k: kernel_roofline(k, c[k], kern[k], wl.dtype) for k in kern}
-    dominant = max(kern, key=lambda k: kern[k])
-    roof = dict(rooflines[dominant])
-    roof["kernel"] = dominant
-    roof["avg_us"] = kern[dominant] * 1e6
-    traffic = measured_traffic(dominant, wl.name)
-    roof["traffic"] = traffic
-    roof = {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "kernel", "avg_us")}
+    def roofline_of(m, kernel="split_attn"):
+        wl, c, kd = m["wl"], m["c"], m["kern"][kernel]
+        roof = kernel_roofline(kernel, c[kernel], kd["mean"], wl.dtype)
+        roof["traffic"] = measured_traffic(kernel, wl.name)
+        cnt = measured_counters(kernel, wl.name)
+        roof["mfma_util"] = cnt.get("mfma_util") if cnt else None
+        roof.update(kernel=kernel, workload=wl.name, avg_us=kd["mean"] * 1e6,
+                    median_us=kd["median"] * 1e6, p10_us=kd["p10"] * 1e6, p90_us=kd["p90"] * 1e6,
+                    runs=kd["n"])
+        return roof
 
+    def entry(m):
+        wl, c = m["wl"], m["c"]
+        t_split = m["kern"]["split_attn"]["mean"]
+        return dict(
+            step_us=m["step_s"] * 1e6, step_tflops=c["step"]["flops"] / m["step_s"] / 1e12,
+            step_hbm_gbps=c["step"]["bytes"] / m["step_s"] / 1e9,
+            graph_step_us=None if m["graph_s"] is None else m["graph_s"] * 1e6,
+            step_dist_us=us(m["step_dist"]),
+            kernels_us={k: us(v) for k, v in m["kern"].items()},
+            splits=m["splits"], chunk_len=m["chunk"], layers_rotated=m["n_layers"],
+            split_us=t_split * 1e6,
+            cache_gbps=c["split_attn"]["bytes"] / t_split / 1e9,
+            cache_plus_partials_gbps=(c["split_attn"]["bytes"] + c["split_attn"]["partial_bytes"])
+            / t_split / 1e9,
+            tflops=c["split_attn"]["flops"] / t_split / 1e12,
+            roofline=roofline_of(m))
+
+    head = measure(args.workload, args.steps, args.warmup)
+    wl, c = head["wl"], head["c"]
+    rooflines = {k: kernel_roofline(k, c[k], v["mean"], wl.dtype) for k, v in head["kern"].items()}
     out = {
         "metric": METRIC,
-        "value": c["step"]["flops"] / step_s / 1e12,
+        "value": c["step"]["flops"] / head["step_s"] / 1e12,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_s * 1e3,
-        "graph_ms_per_step": graph_s * 1e3,
+        "ms_per_step": head["step_s"] * 1e3,
+        "graph_ms_per_step": None if head["graph_s"] is None else head["graph_s"] * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -398,44 +537,28 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "n_q": wl.n_q,
                    "context": int(wl.max_len), "h": wl.h, "d_c": wl.d_c, "d_r": wl.d_r,
-                   "d_h": wl.d_h, "page_size": wl.page_size, "splits": splits,
-                   "chunk_len": chunk, "layers_rotated": n_layers},
-        "cache_gbps": c["step"]["cache_bytes"] / step_s / 1e9,
-        "roofline": roof,
+                   "d_h": wl.d_h, "page_size": wl.page_size, "splits": head["splits"],
+                   "chunk_len": head["chunk"], "layers_rotated": head["n_layers"]},
+        "cache_gbps": c["step"]["cache_bytes"] / head["step_s"] / 1e9,
+        # the split kernel (scores, softmax and latent sums over the cache)
+        # against its roofline at this workload
+        "roofline": roofline_of(head),
         # the whole step against the same HBM peak: the bytes the method must
         # move per step (cache read once, W_UK and W_UV once) over its wall time
-        "step_hbm": dict(algorithmic_bytes=c["step"]["bytes"], achieved=c["step"]["bytes"] / step_s / 1e9,
-                         peak=HBM_GBPS, unit="GB/s", frac=c["step"]["bytes"] / step_s / 1e9 / HBM_GBPS),
-        "kernels": {k: dict(avg_us=kern[k] * 1e6, **rooflines[k]) for k in kern},
+        "step_hbm": dict(algorithmic_bytes=c["step"]["bytes"], achieved=c["step"]["bytes"] / head["step_s"] / 1e9,
+                         peak=HBM_GBPS, unit="GB/s",
+                         frac=c["step"]["bytes"] / head["step_s"] / 1e9 / HBM_GBPS),
+        "timing": dict(step_us=us(head["step_dist"]), runs=dist_runs,
+                       how="per-step events on the launch stream; per-kernel start/stop events "
+                           "recorded by each kernel's dispatch; mean/median/p10/p90 over the runs"),
+        "kernels": {k: dict(us(head["kern"][k]), **rooflines[k]) for k in head["kern"]},
     }
-
-    def split_entry(wl2, c2, kern2, s2, ch2, nl2, step2=None, graph2=None):
-        k = "split_attn"
-        t_split = kern2[k]
-        e = dict(split_us=t_split * 1e6, splits=s2, chunk_len=ch2, layers_rotated=nl2,
-                 cache_gbps=c2["split_attn"]["bytes"] / t_split / 1e9,
-                 cache_plus_partials_gbps=(c2["split_attn"]["bytes"] + c2["split_attn"]["partial_bytes"])
-                 / t_split / 1e9,
-                 tflops=c2["split_attn"]["flops"] / t_split / 1e12,
-                 kernels_us={kk: v * 1e6 for kk, v in kern2.items()},
-                 roofline=dict(kernel_roofline(k, c2[k], t_split, wl2.dtype),
-                               traffic=measured_traffic(k, wl2.name)))
-        if step2 is not None:
-            e.update(step_us=step2 * 1e6, step_tflops=c2["step"]["flops"] / step2 / 1e12,
-                     step_hbm_gbps=c2["step"]["bytes"] / step2 / 1e9, graph_step_us=graph2 * 1e6)
-        return e
-
     sweep = {}
     for name in [n for n in args.extra.split(",") if n]:
-        wl2, dw2, c2, step2, graph2, kern2, s2, ch2, nl2 = measure(name, max(10, args.steps // 2), 5)
-        sweep[wl2.name] = split_entry(wl2, c2, kern2, s2, ch2, nl2, step2, graph2)
-        log("%s: step %.2f us; kernels (us): %s" % (name, step2 * 1e6,
-                                                   {k: round(v * 1e6, 2) for k, v in kern2.items()}))
-        del dw2
+        m = measure(name, max(10, args.steps // 2), 5)
+        sweep[name] = entry(m)
     if sweep:
         out["sweep"] = sweep
-        if "ds2_t32k" in sweep:  # the point the split kernel's roofline bar is set at
-            out["split_kernel_ds2_t32k"] = dict(sweep["ds2_t32k"])
 
     if not args.no_achievable:
         out["achievable"] = achievable_peaks()

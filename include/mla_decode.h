@@ -48,7 +48,16 @@
  *
  * Device-side safety: page ids are clamped into [0, num_pages) and lengths
  * into [0, max_context_len] inside the kernels, so malformed device-side
- * tables give wrong numbers but never an out-of-bounds access.
+ * tables give wrong numbers but never an out-of-bounds access.  This is why
+ * `run` takes the pool's page count (num_pages) beside the problem's own
+ * arguments.
+ *
+ * Thread safety: a plan is immutable after mla_decode_create, except for
+ * its optional timing record: `run` takes the next timing slot with an
+ * atomic increment.  Concurrent runs on one plan (from several threads, on
+ * several streams) are legal when their workspaces (and outputs) are
+ * distinct.  mla_decode_enable_timing, mla_decode_read_timing(_runs) and
+ * mla_decode_destroy must not overlap any other call on the same plan.
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -89,13 +98,19 @@ typedef struct {
 } mla_decode_config_t;
 
 /* Validates the configuration and builds a plan (host only, no device work).
+ * The dimensions are those of the pages' problem statement: h heads, latent
+ * width d_c, decoupled RoPE width d_r and per-head width d_h ("MLA, dim by
+ * dim" section 5.2, the per-head query, key and value shapes); a shape that
+ * no kernel can take is refused here ("Mathematical Prerequisites for
+ * DeepSeek-V2" section 1, the dimension-compatibility rule of products).
  * On success *out_plan owns a plan to release with mla_decode_destroy. */
 mla_status_t mla_decode_create(const mla_decode_config_t* cfg, mla_decode_t* out_plan);
 
 /* Bytes of device workspace `run` needs for this batch shape (0 on an
  * invalid request; the reason is in mla_decode_last_error()).  The
- * workspace holds the absorbed queries and the per-chunk partial results
- * and log-sum-exps (and, on the general path, the merged latents). */
+ * workspace holds the absorbed queries (W_UK[i]^T q, "Mathematical
+ * Prerequisites for DeepSeek-V2" section 6) and the per-chunk partial
+ * results and log-sum-exps (and, on the general path, the merged latents). */
 size_t mla_decode_workspace_size(mla_decode_t plan, int32_t batch, int32_t n_q,
                                  int32_t max_context_len);
 
@@ -111,7 +126,13 @@ mla_status_t mla_decode_split_plan(mla_decode_t plan, int32_t batch, int32_t n_q
                                    int32_t* chunk_len);
 
 /* Enqueues one decode step on `stream` (a hipStream_t; NULL = the null
- * stream).  Every pointer is device memory:
+ * stream): the absorbed-weight decode of "MLA, dim by dim" section 5.2 (the
+ * cached decode chains: scores against the latent and the shared RoPE key
+ * cache, softmax over the visible tokens, latent sum, up-projection) and
+ * "From Vanilla Transformers to Modern LLMs ... Part 3" sections 3.e.2 to
+ * 3.p.  The arguments are that problem's: queries q and q_R, the latent and
+ * RoPE caches (here paged), W_UK, W_UV and the context lengths.  Every
+ * pointer is device memory:
  *   q            [batch][n_q][h][d_h]         dtype
  *   q_r          [batch][n_q][h][d_r]         dtype, already rotated
  *   latent_pool  [num_pages][page_size][d_c]  dtype
@@ -132,7 +153,8 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
                             const void* w_uk, const void* w_uv, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
-/* Per-kernel timing (instrumentation, off by default).  With max_runs > 0
+/* Per-kernel timing (instrumentation, off by default; not part of the
+ * method).  With max_runs > 0
  * every later `run` on this plan launches each of its kernels (absorb,
  * split, combine, up-project) with a start and a stop HIP event that the
  * dispatch itself fills in (the kernel's own begin and end, as a profiler
@@ -147,6 +169,13 @@ mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs);
  * merge and the up-projection run as one kernel, reported in ms[2]; ms[3]
  * is then 0. */
 mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs);
+
+/* Per-run variant of mla_decode_read_timing: writes the milliseconds of
+ * each of the four steps of each recorded run, ms[4 r + k] for run r <
+ * *runs <= max_runs (a step the path does not launch reads 0), then starts
+ * a new recording. */
+mla_status_t mla_decode_read_timing_runs(mla_decode_t plan, float* ms, int32_t max_runs,
+                                         int32_t* runs);
 
 /* Releases a plan.  NULL is accepted and ignored. */
 void mla_decode_destroy(mla_decode_t plan);

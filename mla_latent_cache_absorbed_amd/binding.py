@@ -27,8 +27,9 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_F32 = 1
 
 EXPORTED = ("mla_decode_create", "mla_decode_workspace_size", "mla_decode_split_plan",
-            "mla_decode_run", "mla_decode_enable_timing", "mla_decode_read_timing",
-            "mla_decode_destroy", "mla_decode_last_error")
+            "mla_decode_run", "mla_decode_enable_timing",
+            "mla_decode_read_timing", "mla_decode_read_timing_runs", "mla_decode_destroy",
+            "mla_decode_last_error")
 
 KERNELS = ("q_absorb", "split_attn", "combine", "up_project")
 
@@ -76,6 +77,9 @@ def lib():
         L.mla_decode_enable_timing.restype = ctypes.c_int
         L.mla_decode_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
         L.mla_decode_read_timing.restype = ctypes.c_int
+        L.mla_decode_read_timing_runs.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
+                                                  ctypes.POINTER(i32)]
+        L.mla_decode_read_timing_runs.restype = ctypes.c_int
         L.mla_decode_destroy.argtypes = [vp]
         L.mla_decode_destroy.restype = None
         L.mla_decode_last_error.argtypes = []
@@ -161,6 +165,16 @@ def mla_decode_read_timing(plan):
     runs = ctypes.c_int32()
     _check(lib().mla_decode_read_timing(plan, ms, ctypes.byref(runs)))
     return dict(zip(KERNELS, [float(x) for x in ms])), runs.value
+
+
+def mla_decode_read_timing_runs(plan, max_runs: int):
+    """Per-run milliseconds of each step: a list of dicts (one per recorded
+    run, at most max_runs)."""
+    ms = (ctypes.c_float * (len(KERNELS) * max(1, max_runs)))()
+    runs = ctypes.c_int32()
+    _check(lib().mla_decode_read_timing_runs(plan, ms, max_runs, ctypes.byref(runs)))
+    n = len(KERNELS)
+    return [dict(zip(KERNELS, [float(x) for x in ms[r * n:(r + 1) * n]])) for r in range(runs.value)]
 
 
 def mla_decode_destroy(plan) -> None:

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -29,10 +30,12 @@ struct mla_decode_plan {
   float scale;     // resolved softmax scale
   int num_cus;     // compute units the split heuristic fills
   // optional per-kernel timing: a start and a stop event per kernel per
-  // recorded run, filled in by the launches themselves
+  // recorded run, filled in by the launches themselves.  `run` takes its
+  // slot with an atomic increment (the only thing it changes in a plan), so
+  // concurrent runs on one plan never share a slot.
   std::vector<hipEvent_t> events;
   int timing_capacity = 0;
-  int timing_runs = 0;
+  std::atomic<int> timing_runs{0};
 };
 
 namespace {
@@ -49,9 +52,13 @@ mla_status_t fail(mla_status_t st, const char* fmt, ...) {
   return st;
 }
 
-// A chunk is never shorter than this many tokens unless the context is:
-// each chunk writes h * d_c * 4 bytes of partial result, which must stay
-// small next to the chunk's own cache bytes ((d_c + d_r) * 2 per token).
+// A chunk is never shorter than this many tokens unless the context is.
+// Each chunk writes one partial result per (query token, head): d_c values
+// (bf16 on the fast path: h * d_c * 2 = 128 KB per chunk and query token
+// at h = 128) plus its log-sum-exp, whatever the chunk's length, next to
+// the chunk's (d_c + d_r) * 2 = 1152 bytes of cache per token.  At 128
+// tokens that is 89 % of the chunk's cache bytes, at 256 tokens 44 %: the
+// automatic count below fills the compute units and goes no shorter.
 constexpr int kMinChunkTokens = 128;
 // Work-groups per CU the split kernel is sized for.
 constexpr int kGroupsPerCu = 1;
@@ -171,73 +178,12 @@ mla_status_t check_shape(const mla_decode_plan* p, int32_t batch, int32_t n_q,
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-}  // namespace
-
-extern "C" {
-
-mla_status_t mla_decode_create(const mla_decode_config_t* cfg, mla_decode_t* out_plan) {
-  g_last_error.clear();
-  if (!cfg || !out_plan) return fail(MLA_ERR_INVALID_ARG, "cfg and out_plan must not be NULL");
-  *out_plan = nullptr;
-  const mla_decode_config_t& c = *cfg;
-  if (c.h < 1 || c.d_c < 1 || c.d_h < 1 || c.d_r < 0)
-    return fail(MLA_ERR_INVALID_ARG, "dimensions must be positive (h=%d d_c=%d d_r=%d d_h=%d)",
-                c.h, c.d_c, c.d_r, c.d_h);
-  if (c.dtype != MLA_DTYPE_BF16 && c.dtype != MLA_DTYPE_F32)
-    return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", c.dtype);
-  if (c.out_dtype != -1 && c.out_dtype != MLA_DTYPE_BF16 && c.out_dtype != MLA_DTYPE_F32)
-    return fail(MLA_ERR_INVALID_ARG, "unknown out_dtype %d", c.out_dtype);
-  if (c.page_size < 1 || c.max_batch < 1 || c.max_q_per_seq < 1 || c.max_pages_per_seq < 1)
-    return fail(MLA_ERR_INVALID_ARG,
-                "page_size, max_batch, max_q_per_seq and max_pages_per_seq must be >= 1");
-  if (c.num_splits < 0) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 0");
-  if (!(c.scale >= 0.f) || std::isinf(c.scale))
-    return fail(MLA_ERR_INVALID_ARG, "scale must be finite and >= 0");
-  if ((long long)c.max_pages_per_seq * c.page_size > (1LL << 30))
-    return fail(MLA_ERR_UNSUPPORTED, "context capacity above 2^30 tokens");
-  const bool fast = fast_path_applies(c);
-  if (!fast && c.d_c > 1024)
-    return fail(MLA_ERR_UNSUPPORTED, "d_c=%d: only d_c <= 1024 is built outside the "
-                "(h%%64, 512, 64, 128) bf16 shape", c.d_c);
-
-  mla_decode_plan* p = new (std::nothrow) mla_decode_plan;
-  if (!p) return fail(MLA_ERR_NOMEM, "out of host memory");
-  p->cfg = c;
-  p->out_dtype = c.out_dtype == -1 ? c.dtype : c.out_dtype;
-  p->fast = fast;
-  p->scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)(c.d_h + c.d_r));
-  p->num_cus = query_num_cus();
-  *out_plan = p;
-  return MLA_OK;
-}
-
-size_t mla_decode_workspace_size(mla_decode_t plan, int32_t batch, int32_t n_q,
-                                 int32_t max_context_len) {
-  if (check_shape(plan, batch, n_q, max_context_len) != MLA_OK) return 0;
-  if (batch == 0) return 0;
-  const Split s = plan_splits(*plan, batch, n_q, max_context_len);
-  return layout_for(*plan, batch, n_q, s).total;
-}
-
-mla_status_t mla_decode_split_plan(mla_decode_t plan, int32_t batch, int32_t n_q,
-                                   int32_t max_context_len, int32_t* num_splits,
-                                   int32_t* chunk_len) {
-  mla_status_t st = check_shape(plan, batch, n_q, max_context_len);
-  if (st != MLA_OK) return st;
-  if (!num_splits || !chunk_len) return fail(MLA_ERR_INVALID_ARG, "output pointers are NULL");
-  const Split s = plan_splits(*plan, batch, n_q, max_context_len);
-  *num_splits = s.planned ? 0 : s.splits;
-  *chunk_len = s.planned ? 0 : s.chunk_len;
-  return MLA_OK;
-}
-
-mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
-                            int32_t max_context_len, int32_t num_pages, const void* q,
-                            const void* q_r, const void* latent_pool, const void* rope_pool,
-                            const int32_t* page_table, const int32_t* context_lens,
-                            const void* w_uk, const void* w_uv, void* out, void* workspace,
-                            size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+// One decode step into `workspace` (checked, carved, launched).
+mla_status_t run_impl(mla_decode_t plan, int32_t batch, int32_t n_q, int32_t max_context_len,
+                      int32_t num_pages, const void* q, const void* q_r, const void* latent_pool,
+                      const void* rope_pool, const int32_t* page_table, const int32_t* context_lens,
+                      const void* w_uk, const void* w_uv, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
   mla_status_t st = check_shape(plan, batch, n_q, max_context_len);
   if (st != MLA_OK) return st;
   if (batch == 0) return MLA_OK;  // nothing to do
@@ -306,28 +252,101 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = nullptr;
-  if (plan->timing_runs < plan->timing_capacity)
-    ev = &plan->events[(size_t)plan->timing_runs++ * kEventsPerRun];
+  if (plan->timing_capacity > 0) {
+    const int slot = plan->timing_runs.fetch_add(1);
+    if (slot < plan->timing_capacity) ev = &plan->events[(size_t)slot * kEventsPerRun];
+  }
   for (int k = 0; k < kKernels; ++k) {
-    mla::LaunchCtx c;
-    c.stream = hs;
+    mla::LaunchCtx lc;
+    lc.stream = hs;
     if (ev) {
-      c.start = ev[2 * k];
-      c.stop = ev[2 * k + 1];
+      lc.start = ev[2 * k];
+      lc.stop = ev[2 * k + 1];
     }
     hipError_t e;
     switch (k) {
-      case 0: e = p.fast ? mla::launch_q_absorb_bf16(a, c) : mla::launch_q_absorb_general(a, c); break;
-      case 1: e = p.fast ? mla::launch_split_attn_bf16(a, c) : mla::launch_split_attn_general(a, c); break;
-      case 2: e = p.fast ? mla::launch_finish_bf16(a, c) : mla::launch_combine_general(a, c); break;
+      case 0: e = p.fast ? mla::launch_q_absorb_bf16(a, lc) : mla::launch_q_absorb_general(a, lc); break;
+      case 1: e = p.fast ? mla::launch_split_attn_bf16(a, lc) : mla::launch_split_attn_general(a, lc); break;
+      case 2: e = p.fast ? mla::launch_finish_bf16(a, lc) : mla::launch_combine_general(a, lc); break;
       default:
         if (p.fast) continue;  // folded into the finish kernel
-        e = mla::launch_up_project_general(a, c);
+        e = mla::launch_up_project_general(a, lc);
         break;
     }
     if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   }
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_decode_create(const mla_decode_config_t* cfg, mla_decode_t* out_plan) {
+  g_last_error.clear();
+  if (!cfg || !out_plan) return fail(MLA_ERR_INVALID_ARG, "cfg and out_plan must not be NULL");
+  *out_plan = nullptr;
+  const mla_decode_config_t& c = *cfg;
+  if (c.h < 1 || c.d_c < 1 || c.d_h < 1 || c.d_r < 0)
+    return fail(MLA_ERR_INVALID_ARG, "dimensions must be positive (h=%d d_c=%d d_r=%d d_h=%d)",
+                c.h, c.d_c, c.d_r, c.d_h);
+  if (c.dtype != MLA_DTYPE_BF16 && c.dtype != MLA_DTYPE_F32)
+    return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", c.dtype);
+  if (c.out_dtype != -1 && c.out_dtype != MLA_DTYPE_BF16 && c.out_dtype != MLA_DTYPE_F32)
+    return fail(MLA_ERR_INVALID_ARG, "unknown out_dtype %d", c.out_dtype);
+  if (c.page_size < 1 || c.max_batch < 1 || c.max_q_per_seq < 1 || c.max_pages_per_seq < 1)
+    return fail(MLA_ERR_INVALID_ARG,
+                "page_size, max_batch, max_q_per_seq and max_pages_per_seq must be >= 1");
+  if (c.num_splits < 0) return fail(MLA_ERR_INVALID_ARG, "num_splits must be >= 0");
+  if (!(c.scale >= 0.f) || std::isinf(c.scale))
+    return fail(MLA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if ((long long)c.max_pages_per_seq * c.page_size > (1LL << 30))
+    return fail(MLA_ERR_UNSUPPORTED, "context capacity above 2^30 tokens");
+  const bool fast = fast_path_applies(c);
+  if (!fast && c.d_c > 1024)
+    return fail(MLA_ERR_UNSUPPORTED, "d_c=%d: only d_c <= 1024 is built outside the "
+                "(h%%64, 512, 64, 128) bf16 shape", c.d_c);
+
+  mla_decode_plan* p = new (std::nothrow) mla_decode_plan;
+  if (!p) return fail(MLA_ERR_NOMEM, "out of host memory");
+  p->cfg = c;
+  p->out_dtype = c.out_dtype == -1 ? c.dtype : c.out_dtype;
+  p->fast = fast;
+  p->scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)(c.d_h + c.d_r));
+  p->num_cus = query_num_cus();
+  *out_plan = p;
+  return MLA_OK;
+}
+
+size_t mla_decode_workspace_size(mla_decode_t plan, int32_t batch, int32_t n_q,
+                                 int32_t max_context_len) {
+  if (check_shape(plan, batch, n_q, max_context_len) != MLA_OK) return 0;
+  if (batch == 0) return 0;
+  const Split s = plan_splits(*plan, batch, n_q, max_context_len);
+  return layout_for(*plan, batch, n_q, s).total;
+}
+
+mla_status_t mla_decode_split_plan(mla_decode_t plan, int32_t batch, int32_t n_q,
+                                   int32_t max_context_len, int32_t* num_splits,
+                                   int32_t* chunk_len) {
+  mla_status_t st = check_shape(plan, batch, n_q, max_context_len);
+  if (st != MLA_OK) return st;
+  if (!num_splits || !chunk_len) return fail(MLA_ERR_INVALID_ARG, "output pointers are NULL");
+  const Split s = plan_splits(*plan, batch, n_q, max_context_len);
+  *num_splits = s.planned ? 0 : s.splits;
+  *chunk_len = s.planned ? 0 : s.chunk_len;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
+                            int32_t max_context_len, int32_t num_pages, const void* q,
+                            const void* q_r, const void* latent_pool, const void* rope_pool,
+                            const int32_t* page_table, const int32_t* context_lens,
+                            const void* w_uk, const void* w_uv, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return run_impl(plan, batch, n_q, max_context_len, num_pages, q, q_r, latent_pool, rope_pool,
+                  page_table, context_lens, w_uk, w_uv, out, workspace, workspace_bytes, stream);
 }
 
 mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs) {
@@ -355,29 +374,46 @@ mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs) {
   return MLA_OK;
 }
 
-mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs) {
+mla_status_t mla_decode_read_timing_runs(mla_decode_t plan, float* ms, int32_t max_runs,
+                                         int32_t* runs) {
   g_last_error.clear();
-  if (!plan || !ms || !runs) return fail(MLA_ERR_INVALID_ARG, "NULL argument");
-  for (int k = 0; k < kKernels; ++k) ms[k] = 0.f;
-  const int n = plan->timing_runs;
+  if (!plan || !runs || (max_runs > 0 && !ms) || max_runs < 0)
+    return fail(MLA_ERR_INVALID_ARG, "NULL argument or negative max_runs");
+  const int n = std::min(plan->timing_runs.load(), plan->timing_capacity);
   if (n > 0) {
     // the stop event of the last kernel the plan launches
     const int last = plan->fast ? 2 : 3;
     hipError_t st = hipEventSynchronize(plan->events[(size_t)(n - 1) * kEventsPerRun + 2 * last + 1]);
     if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(st));
   }
-  for (int r = 0; r < n; ++r) {
+  const int keep = std::min(n, max_runs);
+  for (int r = 0; r < keep; ++r) {
     const hipEvent_t* ev = &plan->events[(size_t)r * kEventsPerRun];
     for (int k = 0; k < kKernels; ++k) {
-      if (plan->fast && k == 3) continue;  // no separate up-projection kernel
       float t = 0.f;
-      hipError_t st = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
-      if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(st));
-      ms[k] += t;
+      if (!(plan->fast && k == 3)) {  // no separate up-projection kernel on the fast path
+        hipError_t st = hipEventElapsedTime(&t, ev[2 * k], ev[2 * k + 1]);
+        if (st != hipSuccess) return fail(MLA_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(st));
+      }
+      ms[(size_t)r * kKernels + k] = t;
     }
   }
-  *runs = n;
+  *runs = keep;
   plan->timing_runs = 0;
+  return MLA_OK;
+}
+
+mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs) {
+  g_last_error.clear();
+  if (!plan || !ms || !runs) return fail(MLA_ERR_INVALID_ARG, "NULL argument");
+  const int n = std::min(plan->timing_runs.load(), plan->timing_capacity);
+  std::vector<float> per((size_t)std::max(n, 1) * kKernels, 0.f);
+  mla_status_t st = mla_decode_read_timing_runs(plan, per.data(), n, runs);
+  if (st != MLA_OK) return st;
+  for (int k = 0; k < kKernels; ++k) {
+    ms[k] = 0.f;
+    for (int r = 0; r < *runs; ++r) ms[k] += per[(size_t)r * kKernels + k];
+  }
   return MLA_OK;
 }
 

@@ -27,14 +27,16 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "mla_latent_cache_absorbed_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# MFMA-busy and LDS counters per kernel and workload (same keying)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
-# kernel short name -> (substring of the device symbol, its source file)
+# step name -> (substring of the device symbol, its source files)
 KERNELS = {
-    "q_absorb": ("q_absorb", "q_absorb.hip"),
-    "split_attn": ("split_attn", "split_attn.hip"),
-    "finish": ("finish", "finish.hip"),
-    "combine": ("combine_general", "combine.hip"),
-    "up_project": ("up_general", "general.hip"),
+    "q_absorb": ("q_absorb", ("q_absorb.hip",)),
+    "split_attn": ("split_attn", ("split_attn.hip",)),
+    "finish": ("finish", ("finish.hip",)),
+    "combine": ("combine_general", ("combine.hip",)),
+    "up_project": ("up_general", ("general.hip",)),
 }
 
 
@@ -51,7 +53,7 @@ def source_digest(kernel: str) -> str:
     shared header, comments and layout ignored)."""
     h = hashlib.sha256()
     headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
-    for f in [KERNELS[kernel][1]] + headers:
+    for f in list(KERNELS[kernel][1]) + headers:
         with open(os.path.join(CSRC, f)) as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]

@@ -84,6 +84,8 @@ def lib():
                                                  _ip, _ip, _dp, _dp]
         L.mla_oracle_decode_absorbed.restype = ctypes.c_int
         L.mla_oracle_num_threads.restype = ctypes.c_int
+        L.mla_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.mla_oracle_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -283,3 +285,8 @@ def gather(prob: Problem, b: int, n: int):
 
 def num_threads() -> int:
     return int(lib().mla_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (timing only; results do not depend on it)."""
+    lib().mla_oracle_set_num_threads(int(n))

@@ -240,46 +240,72 @@ void mla_oracle_up_project(int d_h, int d_c, const double* w_uv_i, const double*
 }
 
 /* Same outputs as the explicit form; also returns c_bar[s][m][:] (d_c values)
- * when cbar_out is not NULL. */
+ * when cbar_out is not NULL.  The logical cache of a sequence is gathered
+ * once and shared by all of its selected heads (the steps per head are the
+ * ones above, unchanged). */
 int mla_oracle_decode_absorbed(const mla_oracle_problem_t* P, int n_sel, const int32_t* sel_b,
                                const int32_t* sel_head, double* out, double* cbar_out) {
   int rc = check_problem(P, n_sel, sel_b, sel_head);
   if (rc) return rc;
   const int d_c = P->d_c, d_r = P->d_r, d_h = P->d_h, n_q = P->n_q, h = P->h;
   int fail = 0;
+  char* done = (char*)calloc((size_t)(n_sel > 0 ? n_sel : 1), 1);
+  if (!done) return -5;
 
-#pragma omp parallel for schedule(dynamic, 1)
-  for (int s = 0; s < n_sel; ++s) {
-    const int b = sel_b[s], i = sel_head[s];
+  for (int s0 = 0; s0 < n_sel && !fail; ++s0) {
+    if (done[s0]) continue;
+    const int b = sel_b[s0];
     const int L = P->context_lens[b];
     double* C = (double*)malloc(sizeof(double) * (size_t)L * d_c);
     double* KR = (double*)malloc(sizeof(double) * ((size_t)L * (d_r > 0 ? d_r : 1)));
-    double* sc = (double*)malloc(sizeof(double) * (size_t)L);
-    double* p = (double*)malloc(sizeof(double) * (size_t)L);
-    double* qa = (double*)malloc(sizeof(double) * (size_t)d_c);
-    double* cb = (double*)malloc(sizeof(double) * (size_t)d_c);
-    if (!C || !KR || !sc || !p || !qa || !cb) {
-#pragma omp atomic write
+    if (!C || !KR) {
       fail = 1;
     } else {
       mla_oracle_gather(P, b, L, C, KR);
-      for (int m = 0; m < n_q; ++m) {
-        const size_t row = (size_t)b * n_q + m;
-        const int vis = L - n_q + m + 1;
-        mla_oracle_absorb_query(d_h, d_c, P->w_uk + (size_t)i * d_h * d_c,
-                                P->q + (row * h + i) * d_h, qa);
-        mla_oracle_latent_scores(vis, d_c, d_r, P->scale, qa,
-                                 d_r > 0 ? P->q_r + (row * h + i) * d_r : NULL, C, KR, sc);
-        mla_oracle_softmax(vis, sc, p);
-        mla_oracle_weighted_latent(vis, d_c, p, C, cb);
-        mla_oracle_up_project(d_h, d_c, P->w_uv + (size_t)i * d_h * d_c, cb,
-                              out + ((size_t)s * n_q + m) * d_h);
-        if (cbar_out) memcpy(cbar_out + ((size_t)s * n_q + m) * d_c, cb, sizeof(double) * d_c);
+#pragma omp parallel for schedule(dynamic, 1)
+      for (int s = s0; s < n_sel; ++s) {
+        if (sel_b[s] != b) continue;
+        done[s] = 1; /* each selection is handled by exactly one iteration */
+        const int i = sel_head[s];
+        double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+        double* p = (double*)malloc(sizeof(double) * (size_t)L);
+        double* qa = (double*)malloc(sizeof(double) * (size_t)d_c);
+        double* cb = (double*)malloc(sizeof(double) * (size_t)d_c);
+        if (!sc || !p || !qa || !cb) {
+#pragma omp atomic write
+          fail = 1;
+        } else {
+          for (int m = 0; m < n_q; ++m) {
+            const size_t row = (size_t)b * n_q + m;
+            const int vis = L - n_q + m + 1;
+            mla_oracle_absorb_query(d_h, d_c, P->w_uk + (size_t)i * d_h * d_c,
+                                    P->q + (row * h + i) * d_h, qa);
+            mla_oracle_latent_scores(vis, d_c, d_r, P->scale, qa,
+                                     d_r > 0 ? P->q_r + (row * h + i) * d_r : NULL, C, KR, sc);
+            mla_oracle_softmax(vis, sc, p);
+            mla_oracle_weighted_latent(vis, d_c, p, C, cb);
+            mla_oracle_up_project(d_h, d_c, P->w_uv + (size_t)i * d_h * d_c, cb,
+                                  out + ((size_t)s * n_q + m) * d_h);
+            if (cbar_out) memcpy(cbar_out + ((size_t)s * n_q + m) * d_c, cb, sizeof(double) * d_c);
+          }
+        }
+        free(sc); free(p); free(qa); free(cb);
       }
     }
-    free(C); free(KR); free(sc); free(p); free(qa); free(cb);
+    free(C); free(KR);
   }
+  free(done);
   return fail ? -5 : 0;
+}
+
+/* Sets the number of OpenMP threads later calls use (for timing the oracle
+ * on a given number of cores; results do not depend on it). */
+void mla_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
 }
 
 /* Threads OpenMP will use for the parallel loops above (1 without OpenMP). */

@@ -153,6 +153,25 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
                             const void* w_uk, const void* w_uv, void* out,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * decode step as mla_decode_run, same arguments minus the workspace, with
+ * the workspace taken from a static array in the library's device code
+ * (64 MiB per GPU, held until the process ends; its device address is
+ * looked up once per device).  It calls no hipMalloc, hipFree or other
+ * allocating routine.  A call whose workspace (mla_decode_workspace_size)
+ * exceeds 64 MiB is refused with MLA_ERR_WORKSPACE before anything is
+ * enqueued.  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on a GPU (other streams, other threads, other plans) race and
+ * must be serialised by the caller.  Nothing in the array needs to start
+ * at zero: every byte a step reads was written earlier in the same step. */
+mla_status_t mla_decode_run_static(mla_decode_t plan, int32_t batch, int32_t n_q,
+                                   int32_t max_context_len, int32_t num_pages,
+                                   const void* q, const void* q_r,
+                                   const void* latent_pool, const void* rope_pool,
+                                   const int32_t* page_table, const int32_t* context_lens,
+                                   const void* w_uk, const void* w_uv, void* out, void* stream);
+
 /* Per-kernel timing (instrumentation, off by default; not part of the
  * method).  With max_runs > 0
  * every later `run` on this plan launches each of its kernels (absorb,

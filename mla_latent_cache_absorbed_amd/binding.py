@@ -27,7 +27,7 @@ MLA_DTYPE_BF16 = 0
 MLA_DTYPE_F32 = 1
 
 EXPORTED = ("mla_decode_create", "mla_decode_workspace_size", "mla_decode_split_plan",
-            "mla_decode_run", "mla_decode_enable_timing",
+            "mla_decode_run", "mla_decode_run_static", "mla_decode_enable_timing",
             "mla_decode_read_timing", "mla_decode_read_timing_runs", "mla_decode_destroy",
             "mla_decode_last_error")
 
@@ -73,6 +73,8 @@ def lib():
         L.mla_decode_split_plan.restype = ctypes.c_int
         L.mla_decode_run.argtypes = [vp, i32, i32, i32, i32] + [vp] * 10 + [sz, vp]
         L.mla_decode_run.restype = ctypes.c_int
+        L.mla_decode_run_static.argtypes = [vp, i32, i32, i32, i32] + [vp] * 9 + [vp]
+        L.mla_decode_run_static.restype = ctypes.c_int
         L.mla_decode_enable_timing.argtypes = [vp, i32]
         L.mla_decode_enable_timing.restype = ctypes.c_int
         L.mla_decode_read_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32)]
@@ -153,6 +155,21 @@ def mla_decode_run(plan, batch, n_q, max_context_len, num_pages, q, q_r, latent_
         plan, batch, n_q, max_context_len, num_pages, _ptr(q), _ptr(q_r), _ptr(latent_pool),
         _ptr(rope_pool), _ptr(page_table), _ptr(context_lens), _ptr(w_uk), _ptr(w_uv),
         _ptr(out), _ptr(workspace), workspace_bytes, stream))
+
+
+def mla_decode_run_static(plan, batch, n_q, max_context_len, num_pages, q, q_r, latent_pool,
+                          rope_pool, page_table, context_lens, w_uk, w_uv, out, stream=None) -> int:
+    """Enqueue one decode step with the library's static per-GPU scratch
+    instead of a caller workspace (for callers that cannot allocate)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    return _check(lib().mla_decode_run_static(
+        plan, batch, n_q, max_context_len, num_pages, _ptr(q), _ptr(q_r), _ptr(latent_pool),
+        _ptr(rope_pool), _ptr(page_table), _ptr(context_lens), _ptr(w_uk), _ptr(w_uv),
+        _ptr(out), stream))
 
 
 def mla_decode_enable_timing(plan, max_runs: int) -> None:

@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -178,7 +179,38 @@ mla_status_t check_shape(const mla_decode_plan* p, int32_t batch, int32_t n_q,
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// One decode step into `workspace` (checked, carved, launched).
+// Scratch memory of mla_decode_run_static, for callers that cannot
+// allocate: one array per GPU in the library's code object, held until the
+// process ends.  Host code never hands the array's name to a kernel (on the
+// host it is a stand-in, not a device address): the device address comes
+// from hipGetSymbolAddress, once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call for that device.
+mla_status_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MLA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
+}
+
+// One decode step into `workspace` (checked, carved, launched); shared by
+// mla_decode_run and mla_decode_run_static.
 mla_status_t run_impl(mla_decode_t plan, int32_t batch, int32_t n_q, int32_t max_context_len,
                       int32_t num_pages, const void* q, const void* q_r, const void* latent_pool,
                       const void* rope_pool, const int32_t* page_table, const int32_t* context_lens,
@@ -314,6 +346,12 @@ mla_status_t mla_decode_create(const mla_decode_config_t* cfg, mla_decode_t* out
   p->fast = fast;
   p->scale = c.scale > 0.f ? c.scale : 1.0f / std::sqrt((float)(c.d_h + c.d_r));
   p->num_cus = query_num_cus();
+  int devices = 0;
+  if (hipGetDeviceCount(&devices) == hipSuccess && devices > 0) {
+    void* ws = nullptr;
+    if (static_scratch(&ws) != MLA_OK) g_last_error.clear();  // retried by mla_decode_run_static
+  }
+  (void)hipGetLastError();
   *out_plan = p;
   return MLA_OK;
 }
@@ -347,6 +385,28 @@ mla_status_t mla_decode_run(mla_decode_t plan, int32_t batch, int32_t n_q,
   g_last_error.clear();
   return run_impl(plan, batch, n_q, max_context_len, num_pages, q, q_r, latent_pool, rope_pool,
                   page_table, context_lens, w_uk, w_uv, out, workspace, workspace_bytes, stream);
+}
+
+mla_status_t mla_decode_run_static(mla_decode_t plan, int32_t batch, int32_t n_q,
+                                   int32_t max_context_len, int32_t num_pages, const void* q,
+                                   const void* q_r, const void* latent_pool, const void* rope_pool,
+                                   const int32_t* page_table, const int32_t* context_lens,
+                                   const void* w_uk, const void* w_uv, void* out, void* stream) {
+  g_last_error.clear();
+  mla_status_t st = check_shape(plan, batch, n_q, max_context_len);
+  if (st != MLA_OK) return st;
+  if (batch == 0) return MLA_OK;
+  const size_t need = layout_for(*plan, batch, n_q, plan_splits(*plan, batch, n_q, max_context_len)).total;
+  if (need > kStaticScratchBytes)
+    return fail(MLA_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the static scratch of mla_decode_run_static "
+                "holds %zu (use mla_decode_run with a workspace)",
+                need, kStaticScratchBytes);
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != MLA_OK) return st;
+  return run_impl(plan, batch, n_q, max_context_len, num_pages, q, q_r, latent_pool, rope_pool,
+                  page_table, context_lens, w_uk, w_uv, out, ws, kStaticScratchBytes, stream);
 }
 
 mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs) {

@@ -255,6 +255,22 @@ def kernel_distribution(dw, layers, n):
     return out
 
 
+def launch_floor(dw, layers, n):
+    """Per-kernel times of the same plan and grids with every context length
+    set to 1: all split work-groups but one find no visible token and leave
+    at once, so the split kernel's time is its launch-and-drain floor at this
+    grid (the absorb and finish kernels do their usual work)."""
+    import copy
+    import torch
+    floor = copy.copy(layers)
+    floor.sets = []
+    for s in layers.sets:
+        d = dict(s)
+        d["context_lens"] = torch.ones_like(s["context_lens"])
+        floor.sets.append(d)
+    return kernel_distribution(dw, floor, n)
+
+
 def achievable_peaks():
     """What plain library work reaches on this GPU, for context beside the
     vendor peaks: a 1 GiB device-to-device copy (read + write bytes) and a
@@ -436,6 +452,9 @@ def main():
                     help="skip the copy and GEMM measurements of achievable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the launch-floor runs (context lengths 1), e.g. under a profiler, "
+                         "whose per-kernel averages would include them")
     ap.add_argument("--layers", type=int, default=0, help="0 = enough for 1 GiB")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run plain device-to-device copies of MB MiB (the reference kernel "
@@ -467,7 +486,7 @@ def main():
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
     dist_runs = max(args.dist_runs, args.steps)
 
-    def measure(name, steps, warmup):
+    def measure(name, steps, warmup, with_floor=False):
         wl = inputs.make(name)
         dw = DeviceWorkload(wl)
         n_layers = args.layers or max(2, min(60, math.ceil(MIN_ROTATION_BYTES / layer_bytes(wl))))
@@ -482,10 +501,15 @@ def main():
         log("%s: step %.2f us (mean of %d); median %.2f us over %d; kernels (median us): %s" %
             (name, step_s * 1e6, steps, step_dist["median"] * 1e6, dist_runs,
              {k: round(v["median"] * 1e6, 2) for k, v in kern_dist.items()}))
+        floor = None
+        if with_floor:
+            floor = {k: stats(v) for k, v in launch_floor(dw, layers, dist_runs).items()}
+            log("%s: launch floor (context lengths 1), kernels (median us): %s" %
+                (name, {k: round(v["median"] * 1e6, 2) for k, v in floor.items()}))
         c = counts(wl, chunk_count(wl, splits, chunk, num_cus))
         del layers
         return dict(wl=wl, c=c, step_s=step_s, graph_s=graph_s, step_dist=step_dist, kern=kern_dist,
-                    splits=splits, chunk=chunk, n_layers=n_layers)
+                    splits=splits, chunk=chunk, n_layers=n_layers, floor=floor)
 
     def us(d):
         return {k: d[k] * 1e6 for k in ("mean", "median", "p10", "p90")}
@@ -518,7 +542,7 @@ def main():
             tflops=c["split_attn"]["flops"] / t_split / 1e12,
             roofline=roofline_of(m))
 
-    head = measure(args.workload, args.steps, args.warmup)
+    head = measure(args.workload, args.steps, args.warmup, with_floor=not args.no_floor)
     wl, c = head["wl"], head["c"]
     rooflines = {k: kernel_roofline(k, c[k], v["mean"], wl.dtype) for k, v in head["kern"].items()}
     out = {
@@ -552,6 +576,9 @@ def main():
                        how="per-step events on the launch stream; per-kernel start/stop events "
                            "recorded by each kernel's dispatch; mean/median/p10/p90 over the runs"),
         "kernels": {k: dict(us(head["kern"][k]), **rooflines[k]) for k in head["kern"]},
+        # the same plan and grids with every context length 1 (the split
+        # kernel's launch-and-drain floor at this grid)
+        "launch_floor_us": None if head["floor"] is None else {k: us(v) for k, v in head["floor"].items()},
     }
     sweep = {}
     for name in [n for n in args.extra.split(",") if n]:

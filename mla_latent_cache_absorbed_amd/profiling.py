@@ -12,6 +12,13 @@ Usage (after one counter run each, see the --help text)::
     python -m mla_latent_cache_absorbed_amd.profiling \\
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-bytes N --workload ds2_t4k --command "..."
+
+A second mode records the MFMA and LDS counters of one run (rocprofv3's
+derived metrics MfmaUtil, MfmaFlopsBF16, LdsUtil and LdsBankConflict, and
+the raw counters behind them) in ``profiles/counters.json``::
+
+    python -m mla_latent_cache_absorbed_amd.profiling counters \\
+        --pmc DIR --workload ds2_t32k --command "..."
 """
 from __future__ import annotations
 
@@ -75,6 +82,66 @@ def counter_means(path: str, counter: str) -> dict:
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
+def all_counter_means(path: str) -> dict:
+    """{kernel symbol: {counter: mean over its dispatches}} of every counter
+    in a rocprofv3 --output-format csv directory (or file)."""
+    files = [path] if os.path.isfile(path) else glob.glob(
+        os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError("no counter_collection.csv under %s" % path)
+    vals = defaultdict(lambda: defaultdict(list))
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                vals[row["Kernel_Name"]][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+
+
+# derived metric (rocprofv3's name) -> key in counters.json and its scale
+DERIVED = {
+    "MfmaUtil": ("mfma_util", 0.01),          # percent -> fraction of SIMD cycles with the MFMA busy
+    "MfmaFlopsBF16": ("mfma_flops_bf16", 1.0),
+    "LdsUtil": ("lds_util", 0.01),            # percent -> fraction of CU cycles with LDS indexed work
+    "LdsBankConflict": ("lds_bank_conflicts_per_access", 1.0),
+}
+
+
+def counters_main(argv):
+    ap = argparse.ArgumentParser(prog="profiling counters",
+                                 description="record MFMA / LDS counters of one rocprofv3 --pmc run")
+    ap.add_argument("--pmc", required=True, action="append",
+                    help="rocprofv3 --pmc output directory (repeat for several passes)")
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--command", default="", help="the profiled command, recorded verbatim")
+    ap.add_argument("--out", default=COUNTERS_FILE)
+    args = ap.parse_args(argv)
+    merged = defaultdict(dict)
+    for d in args.pmc:
+        for sym, cs in all_counter_means(d).items():
+            merged[sym].update(cs)
+    try:
+        with open(args.out) as fh:
+            table = json.load(fh)
+    except (OSError, ValueError):
+        table = {}
+    for sym, cs in merged.items():
+        k = short_name(sym)
+        if k is None:
+            continue
+        e = {"source_digest": source_digest(k), "symbol": sym, "command": args.command}
+        for name, (key, scale) in DERIVED.items():
+            if name in cs:
+                e[key] = cs[name] * scale
+        e["raw"] = {c: v for c, v in cs.items() if c not in DERIVED}
+        table.setdefault(k, {})[args.workload] = e
+        print("%-11s %-14s %s" % (k, args.workload, "  ".join(
+            "%s %.4g" % (key, e[key]) for _, (key, _) in DERIVED.items() if key in e)))
+    os.makedirs(os.path.dirname(args.out), exist_ok=True)
+    with open(args.out, "w") as fh:
+        json.dump(table, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
 def short_name(symbol: str):
     for k, (needle, _) in KERNELS.items():
         if needle in symbol:
@@ -134,4 +201,8 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    import sys
+    if len(sys.argv) > 1 and sys.argv[1] == "counters":
+        counters_main(sys.argv[2:])
+    else:
+        main()

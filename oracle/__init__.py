@@ -85,6 +85,8 @@ def lib():
         L.mla_oracle_decode_absorbed.restype = ctypes.c_int
         L.mla_oracle_num_threads.restype = ctypes.c_int
         L.mla_oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.mla_oracle_output_project.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
+        L.mla_oracle_output_project.restype = None
         L.mla_oracle_set_num_threads.restype = None
         _lib = L
     return _lib
@@ -180,6 +182,23 @@ def up_project(w_uv_i, c_bar) -> np.ndarray:
     out = np.empty(d_h)
     lib().mla_oracle_up_project(d_h, d_c, _p(W), _p(c), _p(out))
     return out
+
+
+def output_project(o, w_o) -> np.ndarray:
+    """u = [o_1; ...; o_h] W^O per query row.  ``o`` holds head outputs
+    [..., h, d_h] (as the decode step returns them); each row's heads are
+    concatenated head after head into k = h * d_h values.  ``w_o`` is the
+    pages' k x d matrix.  Returns [..., d]."""
+    W = _f64(w_o)
+    k, d = W.shape
+    o = _f64(o)
+    if o.ndim < 2 or o.shape[-2] * o.shape[-1] != k:
+        raise ValueError("o must be [..., h, d_h] with h * d_h = %d" % k)
+    lead = o.shape[:-2]
+    rows_arr = np.ascontiguousarray(o.reshape(-1, k))
+    out = np.empty((rows_arr.shape[0], d))
+    lib().mla_oracle_output_project(rows_arr.shape[0], k, d, _p(rows_arr), _p(W), _p(out))
+    return out.reshape(tuple(lead) + (d,))
 
 
 # --------------------------------------------------------------------------

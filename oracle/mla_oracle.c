@@ -298,6 +298,39 @@ int mla_oracle_decode_absorbed(const mla_oracle_problem_t* P, int n_sel, const i
   return fail ? -5 : 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Output projection, the step after the decode path.                        */
+/* ------------------------------------------------------------------------ */
+
+/* u = [o_1 ; ... ; o_h] W^O for each of `rows` query rows.  The head
+ * outputs of a row are concatenated head after head into one row vector of
+ * k = h * d_h values and multiplied from the right by the output projection
+ * W^O, a k x d matrix stored row-major ("From Vanilla Transformers to Modern
+ * LLMs ... Part 3" sections 3.h and 3.p; "Multi-Head Latent Attention:
+ * Low-Rank KV Compression, Decoupled RoPE, and Matrix Absorption", section
+ * "Matrix Absorption", where the concatenated head outputs are multiplied by
+ * W^O).  Written as the row vector's combination of the rows of W^O,
+ * u[j] = sum_x o[x] W^O[x][j], summed in increasing x. */
+void mla_oracle_output_project(int rows, int k, int d, const double* o, const double* w_o, double* u) {
+  const int jb = 256;  /* columns per parallel block */
+  const int nblk = (d + jb - 1) / jb;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int j0 = blk * jb, j1 = j0 + jb < d ? j0 + jb : d;
+    for (int r = 0; r < rows; ++r) {
+      double* ur = u + (size_t)r * d;
+      for (int j = j0; j < j1; ++j) ur[j] = 0.0;
+      for (int x = 0; x < k; ++x) {
+        const double ox = o[(size_t)r * k + x];
+        const double* wx = w_o + (size_t)x * d;
+        for (int j = j0; j < j1; ++j) ur[j] += ox * wx[j];
+      }
+    }
+  }
+}
+
 /* Sets the number of OpenMP threads later calls use (for timing the oracle
  * on a given number of cores; results do not depend on it). */
 void mla_oracle_set_num_threads(int n) {

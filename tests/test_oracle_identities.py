@@ -178,3 +178,65 @@ def test_rejects_bad_problems():
     prob = _rand_problem(rng, n_q=3, lens=(2, 6))  # fewer tokens than new queries
     with pytest.raises(ValueError):
         oracle.decode_explicit(prob)
+
+
+# --------------------------------------------------------------------------
+# Output projection (the step after the decode path)
+# --------------------------------------------------------------------------
+def test_output_projection_is_a_matrix_product():
+    """A special case that reduces to a library routine: the concatenated
+    rows times W^O is numpy's matrix product, on random inputs of several
+    shapes, one row or several."""
+    rng = np.random.default_rng(31)
+    for rows, h, d_h, d in ((1, 1, 1, 1), (1, 3, 4, 7), (5, 2, 8, 300), (3, 16, 16, 513)):
+        o = rng.standard_normal((rows, h, d_h))
+        W = rng.standard_normal((h * d_h, d))
+        u = oracle.output_project(o, W)
+        assert u.shape == (rows, d)
+        np.testing.assert_allclose(u, o.reshape(rows, -1) @ W, rtol=1e-12, atol=1e-12)
+
+
+def test_output_projection_small_integers_by_hand():
+    """Brute force on a tiny integer case worked out by hand: one row of two
+    heads with d_h = 2, o_1 = [1, 2] and o_2 = [0, -1], concatenated to
+    k = 4 values, and a 4 x 3 W^O."""
+    o = np.array([[[1.0, 2.0], [0.0, -1.0]]])  # [row][head][d_h]
+    W = np.array([[1.0, 0.0, 2.0],
+                  [0.0, 1.0, 1.0],
+                  [5.0, 5.0, 5.0],
+                  [3.0, -1.0, 0.0]])
+    # u_0 = 1*1 + 2*0 + 0*5 + (-1)*3 = -2;  u_1 = 0 + 2 + 0 + 1 = 3;  u_2 = 2 + 2 + 0 + 0 = 4
+    np.testing.assert_array_equal(oracle.output_project(o, W), [[-2.0, 3.0, 4.0]])
+
+
+def test_output_projection_sums_per_head_blocks():
+    """u = sum_i o_i W^O_i, where W^O_i is the block of d_h rows of W^O that
+    multiplies head i (the per-head form the pages use to merge W^O with
+    W_UV): the concatenated product equals the sum of the per-head ones."""
+    rng = np.random.default_rng(32)
+    h, d_h, d = 5, 6, 11
+    o = rng.standard_normal((2, h, d_h))
+    W = rng.standard_normal((h * d_h, d))
+    whole = oracle.output_project(o, W)
+    per_head = sum(oracle.output_project(o[:, i:i + 1, :], W[i * d_h:(i + 1) * d_h]) for i in range(h))
+    np.testing.assert_allclose(whole, per_head, rtol=1e-12, atol=1e-12)
+
+
+def test_output_projection_merges_with_the_value_up_projection():
+    """W^O_i merged with W_UV[i] (the pages' W^OUV = W_UV W^O per head, in
+    this file's column-vector convention W^OUV_i = W_UV[i]^T W^O_i) applied to
+    c_bar gives the same u as the up-projection followed by W^O."""
+    rng = np.random.default_rng(33)
+    prob = _rand_problem(rng, h=3, d_c=8, d_r=4, d_h=5)
+    o, cbar = oracle.decode_absorbed(prob, return_cbar=True)
+    h, d_h, d_c = prob.w_uv.shape
+    d = 7
+    W = rng.standard_normal((h * d_h, d))
+    u = oracle.output_project(o, W)  # [B, n_q, d]
+    B, n_q = o.shape[:2]
+    assert cbar.shape == (B, n_q, h, d_c)
+    merged = np.zeros((B, n_q, d))
+    for i in range(h):
+        w_ouv = prob.w_uv[i].T @ W[i * d_h:(i + 1) * d_h]  # d_c x d
+        merged += cbar[:, :, i, :] @ w_ouv
+    np.testing.assert_allclose(u, merged, rtol=1e-11, atol=1e-12)

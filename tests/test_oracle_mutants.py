@@ -21,6 +21,10 @@ MUTANTS = [
     ("softmax_max_not_subtracted_wrong_sign", "p[t] = exp(s[t] - mx);", "p[t] = exp(mx - s[t]);"),
     ("page_row_index", "(size_t)(t % P->page_size)) * P->d_c", "(size_t)(t / P->page_size)) * P->d_c"),
     ("scale_ignored", "s[t] = scale * (content + rope);", "s[t] = (content + rope);"),
+    ("output_projection_heads_reversed", "const double ox = o[(size_t)r * k + x];",
+     "const double ox = o[(size_t)r * k + (k - 1 - x)];"),
+    ("output_projection_rows_shifted", "const double* wx = w_o + (size_t)x * d;",
+     "const double* wx = w_o + (size_t)((x + 1) % k) * d;"),
 ]
 
 

@@ -193,8 +193,21 @@ def test_p5_whole_decode_with_rope(form, page_size, permute):
     np.testing.assert_allclose(o, _v(P5["o"]), rtol=0, atol=_tol(P5["o"]))
     # output projection of the next step (u_4 = [o_1; o_2] W^O) -- checks the
     # head order of the output as the page concatenates it
-    u4 = o.reshape(-1) @ _v(P5["W_O"])
+    u4 = oracle.output_project(o, _v(P5["W_O"]))
     np.testing.assert_allclose(u4, _v(P5["u4"]), rtol=0, atol=2 * _tol(P5["u4"]))
+
+
+@pytest.mark.parametrize("which", ["with_rope", "content_only"])
+def test_p5_output_projection_of_the_printed_head_outputs(which):
+    """Section 3.h (content only) and 3.p (with RoPE): u_4 = [o_1; o_2] W^O
+    from the head outputs as printed.  W^O is 0/1, so the printed u_4 follows
+    exactly: its first four entries repeat o_1 and o_2, its fifth is the sum
+    of the first and the last."""
+    g = P5 if which == "with_rope" else P5["content_only"]
+    o = _v(g["o"])  # [[o_1], [o_2]] as printed
+    u4 = oracle.output_project(o, _v(P5["W_O"]))
+    assert u4.shape == (5,)
+    np.testing.assert_allclose(u4, _v(g["u4"]), rtol=0, atol=1e-12)
 
 
 @pytest.mark.parametrize("form", ["explicit", "absorbed"])
@@ -204,7 +217,7 @@ def test_p5_whole_decode_content_only(form):
     fn = oracle.decode_explicit if form == "explicit" else oracle.decode_absorbed
     o = fn(prob)[0, 0]
     np.testing.assert_allclose(o, _v(g["o"]), rtol=0, atol=_tol(g["o"]))
-    u4 = o.reshape(-1) @ _v(P5["W_O"])
+    u4 = oracle.output_project(o, _v(P5["W_O"]))
     np.testing.assert_allclose(u4, _v(g["u4"]), rtol=0, atol=2 * _tol(g["u4"]))
 
 

@@ -28,6 +28,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -271,6 +273,53 @@ def launch_floor(dw, layers, n):
     return kernel_distribution(dw, floor, n)
 
 
+def measure_oproj(rows, runs, warmup):
+    """The output projection u = [o_1; ...; o_h] W^O at DeepSeek-V2 width
+    (k = 16384, d = 5120) for `rows` query rows: per-call events on the
+    launch stream over `runs` calls, rotating over enough device copies of
+    W^O (168 MB each) to exceed 1 GiB, so that the weight comes from HBM."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding, inputs
+    case = inputs.make_oproj(rows, seed=320 + rows)
+    k, d = case["k"], case["d"]
+    o = torch.from_numpy(case["o"].reshape(rows, k).view(np.int16)).view(torch.bfloat16).cuda()
+    w0 = torch.from_numpy(np.ascontiguousarray(case["w_o"].T).view(np.int16)).view(torch.bfloat16).cuda()
+    n = max(2, math.ceil(MIN_ROTATION_BYTES / (w0.numel() * 2)))
+    ws = [w0] + [w0.clone() for _ in range(n - 1)]
+    u = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+    need = binding.mla_oproj_workspace_size(rows, k, d)
+    part = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    L = binding.lib()
+    # argument tuples marshalled once (the checked wrapper's Python work per
+    # call would be comparable to the call itself)
+    binding.mla_oproj_run(rows, k, d, o, ws[0], u, part, need, stream=stream)
+    calls = [(rows, k, d, binding.MLA_DTYPE_BF16, binding.MLA_DTYPE_BF16, o.data_ptr(), w.data_ptr(),
+              u.data_ptr(), part.data_ptr(), need, stream) for w in ws]
+    for i in range(warmup):
+        binding.raise_for_status(L.mla_oproj_run(*calls[i % n]))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * runs)]
+    torch.cuda.synchronize()
+    status = 0
+    for i in range(runs):
+        ev[2 * i].record()
+        status = min(status, L.mla_oproj_run(*calls[i % n]))
+        ev[2 * i + 1].record()
+    binding.raise_for_status(status)
+    torch.cuda.synchronize()
+    t = stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) / 1e3 for i in range(runs)])
+    algo_bytes = 2 * (k * d + rows * k + rows * d)
+    flops = 2 * rows * k * d
+    del ws, w0
+    return dict(rows=rows, k=k, d_model=d, slices=max(1, need // (rows * d * 4)), layers_rotated=n,
+                us={kk: t[kk] * 1e6 for kk in ("mean", "median", "p10", "p90")}, runs=t["n"],
+                algorithmic_bytes=algo_bytes, tflops=flops / t["median"] / 1e12,
+                roofline=dict(bound="hbm", achieved=algo_bytes / t["median"] / 1e9, peak=HBM_GBPS, unit="GB/s",
+                              frac=algo_bytes / t["median"] / 1e9 / HBM_GBPS,
+                              traffic=measured_traffic("oproj", "oproj_r%d" % rows),
+                              what="median over the runs of one call (partial kernel + slice sum)"))
+
+
 def achievable_peaks():
     """What plain library work reaches on this GPU, for context beside the
     vendor peaks: a 1 GiB device-to-device copy (read + write bytes) and a
@@ -452,6 +501,9 @@ def main():
                     help="skip the copy and GEMM measurements of achievable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-oproj", action="store_true", help="skip the output-projection measurement")
+    ap.add_argument("--oproj-only", type=int, default=0, metavar="ROWS",
+                    help="only time the output projection of ROWS rows (for profiling) and print its record")
     ap.add_argument("--no-floor", action="store_true",
                     help="skip the launch-floor runs (context lengths 1), e.g. under a profiler, "
                          "whose per-kernel averages would include them")
@@ -485,6 +537,10 @@ def main():
 
     num_cus = torch.cuda.get_device_properties(0).multi_processor_count
     dist_runs = max(args.dist_runs, args.steps)
+
+    if args.oproj_only:
+        print(json.dumps(measure_oproj(args.oproj_only, dist_runs, args.warmup)))
+        return
 
     def measure(name, steps, warmup, with_floor=False):
         wl = inputs.make(name)
@@ -586,6 +642,12 @@ def main():
         sweep[name] = entry(m)
     if sweep:
         out["sweep"] = sweep
+
+    if not args.no_oproj:
+        # the next step after the decode path, measured on its own: the output
+        # projection of the headline's rows and of the batched configurations'
+        out["oproj"] = {"r%d" % r: measure_oproj(r, dist_runs, 10) for r in (1, 32, 64)}
+        log("oproj (median us): %s" % {k: round(v["us"]["median"], 2) for k, v in out["oproj"].items()})
 
     if not args.no_achievable:
         out["achievable"] = achievable_peaks()

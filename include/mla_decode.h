@@ -196,6 +196,34 @@ mla_status_t mla_decode_read_timing(mla_decode_t plan, float* ms, int32_t* runs)
 mla_status_t mla_decode_read_timing_runs(mla_decode_t plan, float* ms, int32_t max_runs,
                                          int32_t* runs);
 
+/* The output projection that follows the decode step: for each of `rows`
+ * query rows, the h head outputs of `run` (o[r][i][:], d_h values each) are
+ * concatenated head after head into k = h * d_h values and multiplied by
+ * W^O, u[r] = [o[r][0]; ...; o[r][h-1]] W^O ("From Vanilla Transformers to
+ * Modern LLMs ... Part 3" sections 3.h and 3.p; the W^O product of the
+ * "Matrix Absorption" section of "Multi-Head Latent Attention: Low-Rank KV
+ * Compression, Decoupled RoPE, and Matrix Absorption").  Every pointer is
+ * device memory:
+ *   o    [rows][k]        dtype (the output of `run`, [batch][n_q][h][d_h],
+ *                          is this with rows = batch * n_q)
+ *   w_o  [d_model][k]     dtype: W^O transposed (each output feature's k
+ *                          weights contiguous; the pages' W^O is k x d_model)
+ *   u    [rows][d_model]  out_dtype (-1 = dtype)
+ *   workspace             mla_oproj_workspace_size bytes (fp32 partial sums
+ *                          over slices of k; 0 bytes, and NULL allowed, when
+ *                          it returns 0), 256-byte aligned, caller-owned
+ * bf16 storage with d_model % 64 == 0 and k % 512 == 0 runs on MFMA with
+ * fp32 accumulation (16-byte aligned o, w_o and u required); other shapes
+ * and fp32 storage on a plain fp32 kernel.  The result does not depend on
+ * timing (partials are summed in a fixed order).  Enqueued on `stream`
+ * (a hipStream_t, NULL = the null stream); no allocation, no
+ * synchronisation.  Argument errors return a negative status before any
+ * launch, with text from mla_decode_last_error(). */
+size_t mla_oproj_workspace_size(int32_t rows, int32_t k, int32_t d_model, int32_t dtype);
+mla_status_t mla_oproj_run(int32_t rows, int32_t k, int32_t d_model, int32_t dtype, int32_t out_dtype,
+                           const void* o, const void* w_o, void* u, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Releases a plan.  NULL is accepted and ignored. */
 void mla_decode_destroy(mla_decode_t plan);
 

@@ -25,11 +25,12 @@ MLA_ERR_NOMEM = -5
 
 MLA_DTYPE_BF16 = 0
 MLA_DTYPE_F32 = 1
+_DTYPE = {"bf16": MLA_DTYPE_BF16, "f32": MLA_DTYPE_F32}
 
 EXPORTED = ("mla_decode_create", "mla_decode_workspace_size", "mla_decode_split_plan",
             "mla_decode_run", "mla_decode_run_static", "mla_decode_enable_timing",
             "mla_decode_read_timing", "mla_decode_read_timing_runs", "mla_decode_destroy",
-            "mla_decode_last_error")
+            "mla_decode_last_error", "mla_oproj_workspace_size", "mla_oproj_run")
 
 KERNELS = ("q_absorb", "split_attn", "combine", "up_project")
 
@@ -82,6 +83,10 @@ def lib():
         L.mla_decode_read_timing_runs.argtypes = [vp, ctypes.POINTER(ctypes.c_float), i32,
                                                   ctypes.POINTER(i32)]
         L.mla_decode_read_timing_runs.restype = ctypes.c_int
+        L.mla_oproj_workspace_size.argtypes = [i32, i32, i32, i32]
+        L.mla_oproj_workspace_size.restype = sz
+        L.mla_oproj_run.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.mla_oproj_run.restype = ctypes.c_int
         L.mla_decode_destroy.argtypes = [vp]
         L.mla_decode_destroy.restype = None
         L.mla_decode_last_error.argtypes = []
@@ -192,6 +197,63 @@ def mla_decode_read_timing_runs(plan, max_runs: int):
     _check(lib().mla_decode_read_timing_runs(plan, ms, max_runs, ctypes.byref(runs)))
     n = len(KERNELS)
     return [dict(zip(KERNELS, [float(x) for x in ms[r * n:(r + 1) * n]])) for r in range(runs.value)]
+
+
+def mla_oproj_workspace_size(rows: int, k: int, d_model: int, dtype: str = "bf16") -> int:
+    return int(lib().mla_oproj_workspace_size(rows, k, d_model, _DTYPE[dtype]))
+
+
+def mla_oproj_run(rows, k, d_model, o, w_o, u, workspace=None, workspace_bytes=None, dtype="bf16",
+                  out_dtype=None, stream=None) -> int:
+    """Enqueue the output projection u = [o_1; ...; o_h] W^O of ``rows`` query
+    rows (``w_o`` is W^O transposed, [d_model][k]).  Tensors or raw device
+    addresses; ``stream`` defaults to torch's current stream."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    return _check(lib().mla_oproj_run(rows, k, d_model, _DTYPE[dtype],
+                                      -1 if out_dtype is None else _DTYPE[out_dtype], _ptr(o), _ptr(w_o),
+                                      _ptr(u), _ptr(workspace), workspace_bytes, stream))
+
+
+class OutputProjection:
+    """u = [o_1; ...; o_h] W^O on torch tensors: checks shapes, dtypes and
+    placement, keeps a workspace, and calls mla_oproj_run."""
+
+    def __init__(self, k, d_model, dtype="bf16", out_dtype=None):
+        self.k, self.d = int(k), int(d_model)
+        self.dtype, self.out_dtype = dtype, out_dtype or dtype
+        self._ws = None
+
+    def workspace(self, rows, device="cuda"):
+        import torch
+        need = mla_oproj_workspace_size(rows, self.k, self.d, self.dtype)
+        if need == 0:
+            return None
+        if self._ws is None or self._ws.numel() < need or self._ws.device != torch.device(device):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=device)
+        return self._ws
+
+    def run(self, o, w_o, u, stream=None):
+        import torch
+        tdt = {"bf16": torch.bfloat16, "f32": torch.float32}
+        rows = o.numel() // self.k if o.numel() else 0
+        for name, t, shape, dt in (("o", o, None, tdt[self.dtype]), ("w_o", w_o, (self.d, self.k), tdt[self.dtype]),
+                                   ("u", u, None, tdt[self.out_dtype])):
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous CUDA tensor of %s" % (name, dt))
+            if shape is not None and tuple(t.shape) != shape:
+                raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if o.numel() != rows * self.k or u.numel() != rows * self.d:
+            raise ValueError("o must hold rows x k and u rows x d_model values")
+        ws = self.workspace(rows, o.device)
+        return mla_oproj_run(rows, self.k, self.d, o, w_o, u, ws, dtype=self.dtype, out_dtype=self.out_dtype,
+                             stream=stream)
 
 
 def mla_decode_destroy(plan) -> None:

@@ -310,6 +310,19 @@ mla_status_t run_impl(mla_decode_t plan, int32_t batch, int32_t n_q, int32_t max
   return MLA_OK;
 }
 
+// Shared argument check of the output projection's two entry points.
+mla_status_t oproj_check(int32_t rows, int32_t k, int32_t d_model, int32_t dtype, int32_t out_dtype) {
+  if (rows < 0 || k < 1 || d_model < 1)
+    return fail(MLA_ERR_INVALID_ARG, "rows must be >= 0 and k, d_model >= 1 (rows=%d k=%d d_model=%d)", rows,
+                k, d_model);
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (out_dtype != -1 && out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_F32)
+    return fail(MLA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if ((long long)rows * d_model > (1LL << 31) || (long long)k * d_model > (1LL << 40))
+    return fail(MLA_ERR_UNSUPPORTED, "output projection larger than this build indexes");
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -407,6 +420,51 @@ mla_status_t mla_decode_run_static(mla_decode_t plan, int32_t batch, int32_t n_q
   if (st != MLA_OK) return st;
   return run_impl(plan, batch, n_q, max_context_len, num_pages, q, q_r, latent_pool, rope_pool,
                   page_table, context_lens, w_uk, w_uv, out, ws, kStaticScratchBytes, stream);
+}
+
+size_t mla_oproj_workspace_size(int32_t rows, int32_t k, int32_t d_model, int32_t dtype) {
+  g_last_error.clear();
+  if (oproj_check(rows, k, d_model, dtype, -1) != MLA_OK) return 0;
+  return mla::oproj_workspace_bytes(rows, k, d_model, dtype == MLA_DTYPE_BF16);
+}
+
+mla_status_t mla_oproj_run(int32_t rows, int32_t k, int32_t d_model, int32_t dtype, int32_t out_dtype,
+                           const void* o, const void* w_o, void* u, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_last_error.clear();
+  mla_status_t st = oproj_check(rows, k, d_model, dtype, out_dtype);
+  if (st != MLA_OK) return st;
+  if (rows == 0) return MLA_OK;
+  if (!o || !w_o || !u) return fail(MLA_ERR_INVALID_ARG, "o, w_o and u must not be NULL");
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const bool out_bf16 = (out_dtype == -1 ? dtype : out_dtype) == MLA_DTYPE_BF16;
+  const size_t need = mla::oproj_workspace_bytes(rows, k, d_model, bf16);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
+  if (need > 0 && !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (mla::oproj_fast_applies(k, d_model, bf16)) {
+    if (!aligned(o, 16) || !aligned(w_o, 16) || !aligned(u, 16))
+      return fail(MLA_ERR_INVALID_ARG, "bf16 kernels need 16-byte aligned o, w_o and u");
+  } else {
+    const size_t el = bf16 ? 2 : 4;
+    if (!aligned(o, el) || !aligned(w_o, el) || !aligned(u, out_bf16 ? 2 : 4))
+      return fail(MLA_ERR_INVALID_ARG, "misaligned tensor");
+  }
+  mla::OprojLaunch p;
+  p.o = o;
+  p.w = w_o;
+  p.part = workspace;
+  p.u = u;
+  p.rows = rows;
+  p.k = k;
+  p.d = d_model;
+  p.in_bf16 = bf16;
+  p.out_bf16 = out_bf16;
+  mla::LaunchCtx lc;
+  lc.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = mla::launch_oproj(p, lc);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
 }
 
 mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs) {

@@ -86,4 +86,21 @@ hipError_t launch_up_project_general(const DecodeArgs& a, const LaunchCtx& s);
 // Log-sum-exp merge of the f32 chunk results into c_bar (general path).
 hipError_t launch_combine_general(const DecodeArgs& a, const LaunchCtx& s);
 
+// Output projection u = [o_1; ...; o_h] W^O of `rows` query rows (oproj.hip).
+struct OprojLaunch {
+  const void* o;  // [rows][k], k = h d_h
+  const void* w;  // [d][k] (W^O transposed)
+  void* part;     // fp32 slice partials (oproj_workspace_bytes), may be null when that is 0
+  void* u;        // [rows][d]
+  int rows = 0, k = 0, d = 0;
+  bool in_bf16 = true, out_bf16 = true;
+};
+// The MFMA kernels apply (bf16 storage, d % 64 == 0, k % 512 == 0).
+bool oproj_fast_applies(int k, int d, bool bf16);
+// Slices of k (a power of two) the MFMA kernels split the product into.
+int oproj_splits(int rows, int k, int d);
+// fp32 partial bytes the launch needs in OprojLaunch::part (0: none).
+size_t oproj_workspace_bytes(int rows, int k, int d, bool bf16);
+hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s);
+
 }  // namespace mla

@@ -211,3 +211,31 @@ def oracle_problem_kwargs(wl: Workload) -> dict:
                 latent_pool=as_f64(wl, "latent_pool"), rope_pool=as_f64(wl, "rope_pool"),
                 page_table=wl.page_table, context_lens=wl.lens,
                 w_uk=as_f64(wl, "w_uk"), w_uv=as_f64(wl, "w_uv"), scale=wl.scale)
+
+
+# --------------------------------------------------------------------------
+# The output projection that follows the decode step
+# --------------------------------------------------------------------------
+# DeepSeek-V2's model width ("MLA Explained", section "Memory: the concrete
+# numbers").
+D_MODEL = 5120
+
+
+def make_oproj(rows: int, h: int = 128, d_h: int = 128, d_model: int = D_MODEL, dtype: str = "bf16",
+               seed: int = 300) -> dict:
+    """Head outputs o [rows][h][d_h] ~ N(0, 1), then W^O in the pages'
+    orientation, k x d_model with k = h d_h, ~ N(0, 1/k) (variance 1/k, as
+    the other weights: variance 1 / fan-in); drawn in that order.  bf16
+    values travel as their 16-bit patterns, fp32 values as float32."""
+    rng = np.random.default_rng(seed)
+    k = h * d_h
+    o = rng.standard_normal((rows, h, d_h), dtype=np.float32)
+    w = (rng.standard_normal((k, d_model), dtype=np.float32) / np.float32(np.sqrt(k))).astype(np.float32)
+    if dtype == "bf16":
+        return dict(o=bf16_bits(o), w_o=bf16_bits(w), dtype=dtype, rows=rows, k=k, d=d_model)
+    return dict(o=o, w_o=w, dtype=dtype, rows=rows, k=k, d=d_model)
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """bf16 patterns or fp32 values -> float64 (exact)."""
+    return bf16_to_f32(a).astype(np.float64) if dtype == "bf16" else np.asarray(a, dtype=np.float64)

@@ -44,6 +44,7 @@ KERNELS = {
     "finish": ("finish", ("finish.hip",)),
     "combine": ("combine_general", ("combine.hip",)),
     "up_project": ("up_general", ("general.hip",)),
+    "oproj": ("oproj_", ("oproj.hip",)),
 }
 
 
@@ -124,10 +125,17 @@ def counters_main(argv):
             table = json.load(fh)
     except (OSError, ValueError):
         table = {}
+    # where a step name covers several kernels, the one with the most MFMA
+    # FLOPs (the one that does the step's arithmetic) is recorded
+    chosen = {}
     for sym, cs in merged.items():
         k = short_name(sym)
         if k is None:
             continue
+        if k not in chosen or cs.get("MfmaFlopsBF16", 0.0) > merged[chosen[k]].get("MfmaFlopsBF16", 0.0):
+            chosen[k] = sym
+    for k, sym in chosen.items():
+        cs = merged[sym]
         e = {"source_digest": source_digest(k), "symbol": sym, "command": args.command}
         for name, (key, scale) in DERIVED.items():
             if name in cs:
@@ -174,19 +182,25 @@ def main():
             table = json.load(fh)
     except (OSError, ValueError):
         table = {}
+    # a step name may cover several kernels launched once per call each (the
+    # output projection's partial and slice-sum kernels): their per-dispatch
+    # means add up to the bytes of one call
+    per_name = {}
     for sym in fetch:
         k = short_name(sym)
         if k is None or sym not in write:
             continue
-        fb = fetch[sym] * 1024.0 * f_factor
-        wb = write[sym] * 1024.0 * w_factor
+        f0, w0, fr, wr = per_name.get(k, (0.0, 0.0, 0.0, 0.0))
+        per_name[k] = (f0 + fetch[sym] * 1024.0 * f_factor, w0 + write[sym] * 1024.0 * w_factor,
+                       fr + fetch[sym], wr + write[sym])
+    for k, (fb, wb, fraw, wraw) in per_name.items():
         table.setdefault(k, {})[args.workload] = {
             "source_digest": source_digest(k),
             "bytes_per_launch": fb + wb,
             "fetch_bytes": fb,
             "write_bytes": wb,
-            "fetch_kib_raw": fetch[sym],
-            "write_kib_raw": write[sym],
+            "fetch_kib_raw": fraw,
+            "write_kib_raw": wraw,
             "copy_kernel": copy_kernel,
             "fetch_factor": f_factor,
             "write_factor": w_factor,

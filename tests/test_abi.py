@@ -23,7 +23,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_decode_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -184,3 +184,20 @@ def test_last_error_cleared_by_success(L):
     plan = binding.mla_decode_create(ds2())
     assert binding.mla_decode_last_error() == ""
     binding.mla_decode_destroy(plan)
+
+
+def test_output_projection_refuses_bad_calls_on_the_host(L):
+    # before any launch: bad sizes, unknown dtype, NULL tensors, missing workspace
+    assert binding.mla_oproj_workspace_size(1, 16384, 5120) == 16 * 5120 * 4  # 16 slices of k
+    assert binding.mla_oproj_workspace_size(1, 64, 40, "f32") == 0           # plain kernel, no partials
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_oproj_run(1, 0, 5, None, None, None, stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_oproj_run(1, 16384, 5120, None, None, None, stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_oproj_run(1, 16384, 5120, 4096, 4096, 4096, stream=0)
+    assert e.value.status == binding.MLA_ERR_WORKSPACE
+    assert "327680 needed" in binding.mla_decode_last_error()
+    assert binding.mla_oproj_run(0, 16384, 5120, None, None, None, stream=0) == binding.MLA_OK  # nothing to do

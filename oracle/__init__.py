@@ -87,6 +87,16 @@ def lib():
         L.mla_oracle_set_num_threads.argtypes = [ctypes.c_int]
         L.mla_oracle_output_project.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
         L.mla_oracle_output_project.restype = None
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        L.mla_oracle_rope_thetas.argtypes = [ctypes.c_int, ctypes.c_double, _dp]
+        L.mla_oracle_rope_thetas.restype = None
+        L.mla_oracle_rope.argtypes = [ctypes.c_int, _dp, ctypes.c_double, _dp, _dp]
+        L.mla_oracle_rope.restype = None
+        L.mla_oracle_cache_append.argtypes = [ctypes.c_int] * 4 + [_dp] * 3 + [_i32p] * 2 + [_dp, _i32p] + \
+            [ctypes.c_int] * 3 + [_dp, _dp]
+        L.mla_oracle_cache_append.restype = ctypes.c_int
+        L.mla_oracle_query_project.argtypes = [ctypes.c_int] * 6 + [_dp] * 4 + [_i32p] + [_dp] * 3
+        L.mla_oracle_query_project.restype = None
         L.mla_oracle_set_num_threads.restype = None
         _lib = L
     return _lib
@@ -199,6 +209,62 @@ def output_project(o, w_o) -> np.ndarray:
     out = np.empty((rows_arr.shape[0], d))
     lib().mla_oracle_output_project(rows_arr.shape[0], k, d, _p(rows_arr), _p(W), _p(out))
     return out.reshape(tuple(lead) + (d,))
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def rope_thetas(d: int, base: float = 10000.0) -> np.ndarray:
+    """theta_j = base^(-2 j / d), j = 0 .. d/2 - 1."""
+    out = np.empty(d // 2)
+    lib().mla_oracle_rope_thetas(d, float(base), _p(out))
+    return out
+
+
+def rope(x, t, theta) -> np.ndarray:
+    """RoPE of the d-vector x at position t (adjacent pairs)."""
+    x = _f64(x); th = _f64(theta)
+    assert x.ndim == 1 and x.size % 2 == 0 and th.size == x.size // 2
+    y = np.empty_like(x)
+    lib().mla_oracle_rope(x.size, _p(x), float(t), _p(th), _p(y))
+    return y
+
+
+def cache_append(x, w_dkv, w_kr, seq, pos, theta, page_table, page_size, latent_pool, rope_pool):
+    """Write c = W_DKV x and k_R = RoPE(W_KR x, pos) of each new token into
+    the pools (copies of the given pools are returned, the inputs are left
+    alone).  x [n][d_model]; w_dkv [d_c][d_model]; w_kr [d_r][d_model];
+    seq, pos [n]; pools [num_pages][page_size][d_c | d_r]."""
+    x = _f64(x); Wc = _f64(w_dkv); Wr = _f64(w_kr); th = _f64(theta)
+    n, d_model = x.shape
+    d_c, d_r = Wc.shape[0], Wr.shape[0]
+    table = _i32(page_table)
+    lat = np.array(latent_pool, dtype=np.float64, order="C", copy=True)
+    rp = np.array(rope_pool, dtype=np.float64, order="C", copy=True)
+    sq, ps = _i32(seq), _i32(pos)
+    rc = lib().mla_oracle_cache_append(n, d_model, d_c, d_r, _p(x), _p(Wc), _p(Wr),
+                                       sq.ctypes.data_as(_ip), ps.ctypes.data_as(_ip), _p(th),
+                                       table.ctypes.data_as(_ip), table.shape[1], int(page_size), lat.shape[0],
+                                       _p(lat), _p(rp))
+    if rc != 0:
+        raise ValueError("a row's page lies outside the page table or the pool")
+    return lat, rp
+
+
+def query_project(x, w_dq, w_uq, w_qr, pos, theta):
+    """q [n][h][d_h] and q_R [n][h][d_r] of n query rows: c_Q = W_DQ x,
+    q_i = W_UQ[i] c_Q, q_R,i = RoPE(W_QR[i] c_Q, pos)."""
+    x = _f64(x); Wd = _f64(w_dq); Wu = _f64(w_uq); Wr = _f64(w_qr); th = _f64(theta)
+    n, d_model = x.shape
+    d_qc = Wd.shape[0]
+    h, d_h = Wu.shape[:2]
+    d_r = Wr.shape[1]
+    q = np.empty((n, h, d_h)); q_r = np.empty((n, h, d_r))
+    ps = _i32(pos)
+    lib().mla_oracle_query_project(n, d_model, d_qc, h, d_h, d_r, _p(x), _p(Wd), _p(Wu), _p(Wr),
+                                   ps.ctypes.data_as(_ip), _p(th), _p(q), _p(q_r))
+    return q, q_r
 
 
 # --------------------------------------------------------------------------

@@ -331,6 +331,100 @@ void mla_oracle_output_project(int rows, int k, int d, const double* o, const do
   }
 }
 
+/* ------------------------------------------------------------------------ */
+/* Decoupled RoPE and the current token's projections (the steps before the */
+/* decode path: what the cache and the query of a step are made from).      */
+/* ------------------------------------------------------------------------ */
+
+/* theta[j] = base^(-2 j / d) for the d/2 pairs j = 0 .. d/2 - 1: the pages'
+ * theta_j = b^(-2 (j - 1) / d) with 1-based j ("MLA, dim by dim", the RoPE
+ * paragraph of section 4). */
+void mla_oracle_rope_thetas(int d, double base, double* theta) {
+  for (int j = 0; j < d / 2; ++j) theta[j] = pow(base, -2.0 * j / d);
+}
+
+/* Rotary position embedding of a d-vector x at position t: each adjacent
+ * pair (x[2j], x[2j+1]) is rotated by the angle t theta[j],
+ *   y[2j]     = x[2j] cos(t theta_j) - x[2j+1] sin(t theta_j),
+ *   y[2j + 1] = x[2j+1] cos(t theta_j) + x[2j] sin(t theta_j),
+ * the element-wise form x cos + rotate_half(x) sin with rotate_half on
+ * adjacent pairs ("MLA, dim by dim", RoPE paragraph of section 4); for one
+ * pair and theta = pi/2 this is the toy rotation by 90 degrees per position
+ * of "From Vanilla Transformers ... Part 3" (section "What RoPE does"). */
+void mla_oracle_rope(int d, const double* x, double t, const double* theta, double* y) {
+  for (int j = 0; j < d / 2; ++j) {
+    const double a = t * theta[j], c = cos(a), s = sin(a);
+    const double x0 = x[2 * j], x1 = x[2 * j + 1];
+    y[2 * j] = x0 * c - x1 * s;
+    y[2 * j + 1] = x1 * c + x0 * s;
+  }
+}
+
+/* The cache append of one decode step.  For each of n new tokens r with
+ * hidden state x[r] (d_model values), sequence seq[r] and position pos[r]:
+ * the latent c = W_DKV x ([d_c][d_model] acting on a column vector;
+ * "Multi-Head Latent Attention: ...", section "MLA: Low-Rank Key-Value
+ * Joint Compression") and the decoupled RoPE key k_R = RoPE(W_KR x, pos)
+ * ([d_r][d_model]; "MLA, dim by dim" section 5.2, the shared key cached
+ * after rotation; "From Vanilla Transformers ..." sections 3.b and 3.k) go
+ * to row pos % page_size of page page_table[seq][pos / page_size] of the
+ * latent and RoPE pools.  Returns 0, or -1 when a row's page lies outside
+ * the table or the pool. */
+int mla_oracle_cache_append(int n, int d_model, int d_c, int d_r, const double* x, const double* w_dkv,
+                            const double* w_kr, const int32_t* seq, const int32_t* pos, const double* theta,
+                            const int32_t* page_table, int max_pages, int page_size, int num_pages,
+                            double* latent_pool, double* rope_pool) {
+  double* kr = (double*)malloc(sizeof(double) * (size_t)(d_r > 0 ? d_r : 1));
+  int rc = 0;
+  for (int r = 0; r < n && rc == 0; ++r) {
+    const int j = pos[r] / page_size;
+    const int page = (pos[r] >= 0 && j < max_pages) ? page_table[(size_t)seq[r] * max_pages + j] : -1;
+    if (page < 0 || page >= num_pages) {
+      rc = -1;
+      break;
+    }
+    const size_t row = (size_t)page * page_size + (size_t)(pos[r] % page_size);
+    const double* xr = x + (size_t)r * d_model;
+    mla_oracle_matvec(d_c, d_model, w_dkv, xr, latent_pool + row * d_c);
+    if (d_r > 0) {
+      mla_oracle_matvec(d_r, d_model, w_kr, xr, kr);
+      mla_oracle_rope(d_r, kr, (double)pos[r], theta, rope_pool + row * d_r);
+    }
+  }
+  free(kr);
+  return rc;
+}
+
+/* The query side of one decode step, for each of n query rows r with
+ * hidden state x[r] and position pos[r]: the query latent c_Q = W_DQ x
+ * ([d_qc][d_model]), then per head i the content query q_i = W_UQ[i] c_Q
+ * ([h][d_h][d_qc]) and the RoPE query q_R,i = RoPE(W_QR[i] c_Q, pos)
+ * ([h][d_r][d_qc]) ("Multi-Head Latent Attention: ...", the query
+ * down-projection and per-head up-projections; "MLA, dim by dim" section
+ * 4.3, the order (X W_DQ) W_UQ; "From Vanilla Transformers ..." sections
+ * 3.d and 3.l).  q is [n][h][d_h], q_r [n][h][d_r]. */
+void mla_oracle_query_project(int n, int d_model, int d_qc, int h, int d_h, int d_r, const double* x,
+                              const double* w_dq, const double* w_uq, const double* w_qr, const int32_t* pos,
+                              const double* theta, double* q, double* q_r) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+  for (int r = 0; r < n; ++r) {
+    double* cq = (double*)malloc(sizeof(double) * (size_t)d_qc);
+    double* qr0 = (double*)malloc(sizeof(double) * (size_t)(d_r > 0 ? d_r : 1));
+    mla_oracle_matvec(d_qc, d_model, w_dq, x + (size_t)r * d_model, cq);
+    for (int i = 0; i < h; ++i) {
+      mla_oracle_matvec(d_h, d_qc, w_uq + (size_t)i * d_h * d_qc, cq, q + ((size_t)r * h + i) * d_h);
+      if (d_r > 0) {
+        mla_oracle_matvec(d_r, d_qc, w_qr + (size_t)i * d_r * d_qc, cq, qr0);
+        mla_oracle_rope(d_r, qr0, (double)pos[r], theta, q_r + ((size_t)r * h + i) * d_r);
+      }
+    }
+    free(cq);
+    free(qr0);
+  }
+}
+
 /* Sets the number of OpenMP threads later calls use (for timing the oracle
  * on a given number of cores; results do not depend on it). */
 void mla_oracle_set_num_threads(int n) {

@@ -240,3 +240,77 @@ def test_output_projection_merges_with_the_value_up_projection():
         w_ouv = prob.w_uv[i].T @ W[i * d_h:(i + 1) * d_h]  # d_c x d
         merged += cbar[:, :, i, :] @ w_ouv
     np.testing.assert_allclose(u, merged, rtol=1e-11, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Decoupled RoPE and the current-token projections
+# --------------------------------------------------------------------------
+def test_rope_frequencies_closed_form():
+    """theta_j = b^(-2 (j - 1) / d) ("MLA, dim by dim", RoPE paragraph)."""
+    np.testing.assert_allclose(oracle.rope_thetas(4, 10000.0), [1.0, 0.01], rtol=1e-15)
+    np.testing.assert_allclose(oracle.rope_thetas(8, 2.0), [1.0, 2 ** -0.25, 2 ** -0.5, 2 ** -0.75], rtol=1e-15)
+    np.testing.assert_allclose(oracle.rope_thetas(64, 10000.0)[-1], 10000.0 ** (-62 / 64), rtol=1e-15)
+
+
+def test_rope_is_a_rotation_per_pair():
+    rng = np.random.default_rng(41)
+    th = oracle.rope_thetas(16, 10000.0)
+    x = rng.standard_normal(16)
+    np.testing.assert_allclose(oracle.rope(x, 0, th), x, rtol=0, atol=0)  # position 0: identity
+    for t in (1, 7, 100000):
+        y = oracle.rope(x, t, th)
+        for j in range(8):  # each adjacent pair keeps its length and turns by t theta_j
+            a, b = x[2 * j:2 * j + 2], y[2 * j:2 * j + 2]
+            assert abs(np.hypot(*a) - np.hypot(*b)) < 1e-12
+            ang = math.atan2(b[1], b[0]) - math.atan2(a[1], a[0])
+            assert abs(math.remainder(ang - t * th[j], 2 * math.pi)) < 1e-9
+        # composition: rotating by a then by b is rotating by a + b
+        np.testing.assert_allclose(oracle.rope(oracle.rope(x, t, th), 5, th), oracle.rope(x, t + 5, th),
+                                   rtol=1e-10, atol=1e-12)
+
+
+def test_rope_scores_depend_on_distance_only():
+    """("From Vanilla Transformers ..." section 3.n): the score of a query at
+    position t and a key at j equals the score of the query turned by t - j
+    against the unrotated key."""
+    rng = np.random.default_rng(42)
+    th = oracle.rope_thetas(64, 10000.0)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for t, j in ((3, 2), (101, 100), (5000, 17)):
+        left = oracle.dot(oracle.rope(q, t, th), oracle.rope(k, j, th))
+        right = oracle.dot(oracle.rope(q, t - j, th), k)
+        assert abs(left - right) <= 1e-10 * max(1.0, abs(left))
+
+
+def test_cache_append_matches_matrix_products_and_paging():
+    rng = np.random.default_rng(43)
+    n, d_model, d_c, d_r, ps = 6, 9, 5, 4, 2
+    x = rng.standard_normal((n, d_model))
+    Wc, Wr = rng.standard_normal((d_c, d_model)), rng.standard_normal((d_r, d_model))
+    th = oracle.rope_thetas(d_r, 10000.0)
+    seq = np.array([0, 0, 1, 1, 1, 0], np.int32)
+    pos = np.array([0, 1, 0, 1, 2, 2], np.int32)
+    table = np.array([[3, 0], [1, 2]], np.int32)
+    lat, rp = oracle.cache_append(x, Wc, Wr, seq, pos, th, table, ps, np.zeros((4, ps, d_c)), np.zeros((4, ps, d_r)))
+    for r in range(n):
+        page, row = table[seq[r], pos[r] // ps], pos[r] % ps
+        np.testing.assert_allclose(lat[page, row], Wc @ x[r], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rp[page, row], oracle.rope(Wr @ x[r], pos[r], th), rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):  # a position past the page table
+        oracle.cache_append(x[:1], Wc, Wr, [0], [4], th, table, ps, np.zeros((4, ps, d_c)), np.zeros((4, ps, d_r)))
+
+
+def test_query_side_matches_matrix_products():
+    rng = np.random.default_rng(44)
+    n, d_model, d_qc, h, d_h, d_r = 3, 10, 6, 4, 5, 4
+    x = rng.standard_normal((n, d_model))
+    Wd = rng.standard_normal((d_qc, d_model))
+    Wu, Wr = rng.standard_normal((h, d_h, d_qc)), rng.standard_normal((h, d_r, d_qc))
+    pos = np.array([0, 9, 123], np.int32)
+    th = oracle.rope_thetas(d_r, 10000.0)
+    q, q_r = oracle.query_project(x, Wd, Wu, Wr, pos, th)
+    for r in range(n):
+        cq = Wd @ x[r]
+        for i in range(h):
+            np.testing.assert_allclose(q[r, i], Wu[i] @ cq, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(q_r[r, i], oracle.rope(Wr[i] @ cq, pos[r], th), rtol=1e-12, atol=1e-12)

@@ -25,6 +25,14 @@ MUTANTS = [
      "const double ox = o[(size_t)r * k + (k - 1 - x)];"),
     ("output_projection_rows_shifted", "const double* wx = w_o + (size_t)x * d;",
      "const double* wx = w_o + (size_t)((x + 1) % k) * d;"),
+    ("rope_sine_sign", "y[2 * j] = x0 * c - x1 * s;", "y[2 * j] = x0 * c + x1 * s;"),
+    ("rope_pairs_are_halves", "const double x0 = x[2 * j], x1 = x[2 * j + 1];",
+     "const double x0 = x[j], x1 = x[j + d / 2];"),
+    ("rope_frequency_exponent", "theta[j] = pow(base, -2.0 * j / d);", "theta[j] = pow(base, -1.0 * j / d);"),
+    ("cache_append_page_row", "const size_t row = (size_t)page * page_size + (size_t)(pos[r] % page_size);",
+     "const size_t row = (size_t)page * page_size + (size_t)(pos[r] / page_size % page_size);"),
+    ("query_side_head_stride", "mla_oracle_matvec(d_h, d_qc, w_uq + (size_t)i * d_h * d_qc, cq,",
+     "mla_oracle_matvec(d_h, d_qc, w_uq + (size_t)(i % 1) * d_h * d_qc, cq,"),
 ]
 
 

@@ -238,3 +238,76 @@ def test_p5_absorbed_returns_cbar():
     prob = _toy_problem()
     _, cb = oracle.decode_absorbed(prob, return_cbar=True)
     np.testing.assert_allclose(cb[0, 0], _v(P5["c_bar"]), rtol=0, atol=_tol(P5["c_bar"]))
+
+
+# --------------------------------------------------------------------------
+# The current-token projections of the toy (the cache rows and the query
+# the decode step reads), and the whole chain from the hidden states to u_4
+# --------------------------------------------------------------------------
+PJ = _load("p5_toy_projections.json")
+_HID = _v(PJ["hidden"])
+_POS = np.asarray(PJ["positions"]["value"], dtype=np.int32)
+_THETA_TOY = np.array([math.pi / 2])  # one pair, 90 degrees per position
+
+
+def _heads_of(m):
+    """A d_model x (h d) page matrix whose head i owns columns d i .. d i + d - 1
+    -> [h][d][d_model] (column-vector convention)."""
+    m = np.asarray(m, dtype=np.float64)
+    return np.stack([m[:, 2 * i:2 * i + 2].T for i in range(m.shape[1] // 2)])
+
+
+def test_p5_rope_rotations():
+    """Sections 3.k, 3.l and 3.i: 90 degrees per position."""
+    for t, (k0, k1) in enumerate(zip(_v(PJ["rope_keys_unrotated"]), _v(PJ["rope_keys_rotated"]))):
+        np.testing.assert_allclose(oracle.rope(k0, t, _THETA_TOY), k1, rtol=0, atol=1e-12)
+    for q0, q1 in zip(_v(PJ["q_rope_unrotated"]), _v(PJ["q_rope_rotated"])):
+        np.testing.assert_allclose(oracle.rope(q0, 3, _THETA_TOY), q1, rtol=0, atol=1e-12)
+    for steps, q1 in zip((3, 2, 1, 0), _v(PJ["q_head1_rotated_by_distance"])):
+        np.testing.assert_allclose(oracle.rope([1, 2], steps, _THETA_TOY), q1, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("page_size,permute", [(4, False), (1, True), (2, True)])
+def test_p5_cache_append(page_size, permute):
+    """Sections 3.b and 3.k: the four tokens' latents and rotated RoPE keys
+    land in their pages."""
+    pages = 4 // page_size
+    order = np.random.default_rng(3).permutation(pages) if permute else np.arange(pages)
+    table = order.reshape(1, pages).astype(np.int32)
+    lat0 = np.full((pages, page_size, 2), np.nan)
+    rp0 = np.full((pages, page_size, 2), np.nan)
+    lat, rp = oracle.cache_append(_HID, _v(PJ["W_DKV"]).T, _v(PJ["W_KR"]).T, np.zeros(4, np.int32), _POS,
+                                  _THETA_TOY, table, page_size, lat0, rp0)
+    for t in range(4):
+        page, row = table[0, t // page_size], t % page_size
+        np.testing.assert_allclose(lat[page, row], _v(PJ["latents"])[t], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(rp[page, row], _v(PJ["rope_keys_rotated"])[t], rtol=0, atol=1e-12)
+    assert np.isnan(lat0).all()  # the inputs are left alone
+
+
+def test_p5_query_side():
+    """Sections 3.d and 3.l: the query of token 4 (position 3), with the
+    toy's query latent equal to the hidden state."""
+    q, q_r = oracle.query_project(_HID[3:4], np.eye(5), _heads_of(PJ["W_Q"]["value"]),
+                                  _heads_of(PJ["W_QR"]["value"]), np.array([3], np.int32), _THETA_TOY)
+    np.testing.assert_allclose(q[0], _v(PJ["q"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(q_r[0], _v(PJ["q_rope_rotated"]), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("form", ["explicit", "absorbed"])
+def test_p5_from_hidden_states_to_u4(form):
+    """The whole toy step from the hidden states: cache append (3.b, 3.k),
+    query side (3.d, 3.l), decode with scale 1/2 (3.o, 3.p) and the output
+    projection (3.p): the printed o and u_4."""
+    table = np.array([[2, 0, 3, 1]], np.int32)  # one token per page, shuffled
+    lat, rp = oracle.cache_append(_HID, _v(PJ["W_DKV"]).T, _v(PJ["W_KR"]).T, np.zeros(4, np.int32), _POS,
+                                  _THETA_TOY, table, 1, np.zeros((4, 1, 2)), np.zeros((4, 1, 2)))
+    q, q_r = oracle.query_project(_HID[3:4], np.eye(5), _heads_of(PJ["W_Q"]["value"]),
+                                  _heads_of(PJ["W_QR"]["value"]), np.array([3], np.int32), _THETA_TOY)
+    prob = oracle.Problem(q=q.reshape(1, 1, 2, 2), q_r=q_r.reshape(1, 1, 2, 2), latent_pool=lat, rope_pool=rp,
+                          page_table=table, context_lens=np.array([4], np.int32), w_uk=W_UK, w_uv=W_UV, scale=0.5)
+    fn = oracle.decode_explicit if form == "explicit" else oracle.decode_absorbed
+    o = fn(prob)[0, 0]
+    np.testing.assert_allclose(o, _v(P5["o"]), rtol=0, atol=_tol(P5["o"]))
+    np.testing.assert_allclose(oracle.output_project(o, _v(P5["W_O"])), _v(P5["u4"]), rtol=0,
+                               atol=2 * _tol(P5["u4"]))

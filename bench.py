@@ -320,6 +320,87 @@ def measure_oproj(rows, runs, warmup):
                               what="median over the runs of one call (partial kernel + slice sum)"))
 
 
+def measure_projections(rows, runs, warmup):
+    """The current token's projections at DeepSeek-V2 widths (d_model 5120,
+    d_c 512, d_r 64, d_qc 1536, 128 heads of 128) for `rows` new tokens: the
+    cache append (into a 512-page pool) and the query side, each timed per
+    call with events on the launch stream over `runs` calls, rotating over
+    enough device copies of its weights to exceed 1 GiB."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding, inputs
+    case = inputs.make_projections(rows, seed=480 + rows)
+    d_model, d_c, d_r, d_qc, h, d_h = (case[k] for k in ("d_model", "d_c", "d_r", "d_qc", "h", "d_h"))
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x = dev(case["x"])
+    stream = torch.cuda.current_stream().cuda_stream
+    L = binding.lib()
+
+    def timed(calls, fn):
+        for i in range(warmup):
+            binding.raise_for_status(fn(*calls[i % len(calls)]))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * runs)]
+        torch.cuda.synchronize()
+        status = 0
+        for i in range(runs):
+            ev[2 * i].record()
+            status = min(status, fn(*calls[i % len(calls)]))
+            ev[2 * i + 1].record()
+        binding.raise_for_status(status)
+        torch.cuda.synchronize()
+        return stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) / 1e3 for i in range(runs)])
+
+    def record(t, algo_bytes, flops, n):
+        return dict(rows=rows, us={kk: t[kk] * 1e6 for kk in ("mean", "median", "p10", "p90")}, runs=t["n"],
+                    weight_copies=n, algorithmic_bytes=algo_bytes, tflops=flops / t["median"] / 1e12,
+                    roofline=dict(bound="hbm", achieved=algo_bytes / t["median"] / 1e9, peak=HBM_GBPS, unit="GB/s",
+                                  frac=algo_bytes / t["median"] / 1e9 / HBM_GBPS,
+                                  what="median over the runs of one call"))
+
+    out = {}
+    # cache append: one token per row at distinct positions of one sequence
+    page_size, pages = 64, 512
+    table = torch.arange(pages, dtype=torch.int32, device="cuda").reshape(1, pages)
+    seq = torch.zeros(rows, dtype=torch.int32, device="cuda")
+    pos = torch.from_numpy(np.random.default_rng(481).choice(pages * page_size, rows, replace=False)
+                           .astype(np.int32)).cuda()
+    lat = torch.zeros((pages, page_size, d_c), dtype=torch.bfloat16, device="cuda")
+    rp = torch.zeros((pages, page_size, d_r), dtype=torch.bfloat16, device="cuda")
+    w_bytes = (d_c + d_r) * d_model * 2
+    n = max(2, math.ceil(MIN_ROTATION_BYTES / w_bytes))
+    w0 = (dev(case["w_dkv"]), dev(case["w_kr"]))
+    ws = [w0] + [(w0[0].clone(), w0[1].clone()) for _ in range(n - 1)]
+    need = binding.mla_cache_append_workspace_size(rows, d_model, d_c, d_r)
+    work = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    calls = [(rows, d_model, d_c, d_r, binding.MLA_DTYPE_BF16, x.data_ptr(), a.data_ptr(), b.data_ptr(),
+              seq.data_ptr(), pos.data_ptr(), table.data_ptr(), pages, page_size, pages, lat.data_ptr(),
+              rp.data_ptr(), None, 10000.0, work.data_ptr(), need, stream) for a, b in ws]
+    t = timed(calls, L.mla_cache_append_run)
+    out["cache_append"] = record(t, w_bytes + rows * d_model * 2 + rows * (d_c + d_r) * 2,
+                                 2 * rows * d_model * (d_c + d_r), n)
+    del ws, lat, rp
+    # query side
+    q = torch.empty((rows, h, d_h), dtype=torch.bfloat16, device="cuda")
+    q_r = torch.empty((rows, h, d_r), dtype=torch.bfloat16, device="cuda")
+    qpos = torch.from_numpy(np.random.default_rng(482).integers(0, 131072, rows).astype(np.int32)).cuda()
+    w_bytes = (d_qc * d_model + h * (d_h + d_r) * d_qc) * 2
+    n = max(2, math.ceil(MIN_ROTATION_BYTES / w_bytes))
+    w0 = (dev(case["w_dq"]), dev(case["w_uq"]), dev(case["w_qr"]))
+    ws = [w0] + [tuple(w.clone() for w in w0) for _ in range(n - 1)]
+    need = binding.mla_query_project_workspace_size(rows, d_model, d_qc, h, d_h, d_r)
+    work = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    calls = [(rows, d_model, d_qc, h, d_h, d_r, binding.MLA_DTYPE_BF16, x.data_ptr(), a.data_ptr(), b.data_ptr(),
+              c.data_ptr(), qpos.data_ptr(), q.data_ptr(), q_r.data_ptr(), None, 10000.0, work.data_ptr(), need,
+              stream) for a, b, c in ws]
+    t = timed(calls, L.mla_query_project_run)
+    out["query_project"] = record(t, w_bytes + rows * d_model * 2 + rows * h * (d_h + d_r) * 2,
+                                  2 * rows * (d_qc * d_model + h * (d_h + d_r) * d_qc), n)
+    del ws
+    return out
+
+
 def achievable_peaks():
     """What plain library work reaches on this GPU, for context beside the
     vendor peaks: a 1 GiB device-to-device copy (read + write bytes) and a
@@ -502,6 +583,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-oproj", action="store_true", help="skip the output-projection measurement")
+    ap.add_argument("--no-projections", action="store_true",
+                    help="skip the cache-append and query-side measurements")
+    ap.add_argument("--projections-only", type=int, default=0, metavar="ROWS",
+                    help="only time the cache append and the query side of ROWS rows and print their records")
     ap.add_argument("--oproj-only", type=int, default=0, metavar="ROWS",
                     help="only time the output projection of ROWS rows (for profiling) and print its record")
     ap.add_argument("--no-floor", action="store_true",
@@ -540,6 +625,9 @@ def main():
 
     if args.oproj_only:
         print(json.dumps(measure_oproj(args.oproj_only, dist_runs, args.warmup)))
+        return
+    if args.projections_only:
+        print(json.dumps(measure_projections(args.projections_only, dist_runs, args.warmup)))
         return
 
     def measure(name, steps, warmup, with_floor=False):
@@ -648,6 +736,12 @@ def main():
         # projection of the headline's rows and of the batched configurations'
         out["oproj"] = {"r%d" % r: measure_oproj(r, dist_runs, 10) for r in (1, 32, 64)}
         log("oproj (median us): %s" % {k: round(v["us"]["median"], 2) for k, v in out["oproj"].items()})
+    if not args.no_projections:
+        # the steps before the decode path, measured on their own: the cache
+        # append and the query side of one and of 64 new tokens
+        out["projections"] = {"r%d" % r: measure_projections(r, dist_runs, 10) for r in (1, 64)}
+        log("projections (median us): %s" % {k: {kk: round(vv["us"]["median"], 2) for kk, vv in v.items()}
+                                             for k, v in out["projections"].items()})
 
     if not args.no_achievable:
         out["achievable"] = achievable_peaks()

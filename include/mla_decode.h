@@ -224,6 +224,68 @@ mla_status_t mla_oproj_run(int32_t rows, int32_t k, int32_t d_model, int32_t dty
                            const void* o, const void* w_o, void* u, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* The cache append of one decode step, before `run` reads the cache: for
+ * each of `rows` new tokens, with hidden state x[r] (d_model values),
+ * sequence seq[r] and position pos[r] (0-based), the latent
+ * c = W_DKV x[r] and the decoupled RoPE key k_R = RoPE(W_KR x[r], pos[r])
+ * are written into row pos % page_size of page
+ * page_table[seq][pos / page_size] of latent_pool and rope_pool
+ * ("Multi-Head Latent Attention: Low-Rank KV Compression, Decoupled RoPE,
+ * and Matrix Absorption", section "MLA: Low-Rank Key-Value Joint
+ * Compression"; "MLA, dim by dim" section 5.2, the shared RoPE key cached
+ * after rotation; "From Vanilla Transformers to Modern LLMs ... Part 3"
+ * sections 3.b and 3.k).  RoPE turns adjacent pairs (y_2j, y_2j+1) by the
+ * angle pos * theta_j, theta_j = rope_theta[j] when rope_theta (device,
+ * d_r / 2 doubles) is given, else rope_base^(-2 j / d_r) ("MLA, dim by
+ * dim", RoPE paragraph of section 4); angles are formed in fp64.  Device
+ * memory, all in `dtype` unless noted:
+ *   x        [rows][d_model]
+ *   w_dkv    [d_c][d_model]   (acting on column vectors: c = W_DKV x)
+ *   w_kr     [d_r][d_model]
+ *   seq, pos [rows] int32;  page_table [batch][max_pages_per_seq] int32
+ *   latent_pool [num_pages][page_size][d_c], rope_pool [num_pages][page_size][d_r]
+ *   workspace   mla_cache_append_workspace_size bytes (NULL when 0), 256-byte aligned
+ * A row whose position or page lies outside the table or the pool is not
+ * written.  bf16 with d_model % 512 == 0 and d_c, d_r multiples of 64 runs
+ * on MFMA (16-byte aligned tensors); other shapes and fp32 on a plain
+ * kernel.  Rows that write the same pool row race.  Enqueued on `stream`;
+ * no allocation, no synchronisation; argument errors return a negative
+ * status before any launch. */
+size_t mla_cache_append_workspace_size(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t dtype);
+mla_status_t mla_cache_append_run(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t dtype,
+                                  const void* x, const void* w_dkv, const void* w_kr,
+                                  const int32_t* seq, const int32_t* pos, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, int32_t page_size, int32_t num_pages,
+                                  void* latent_pool, void* rope_pool, const double* rope_theta,
+                                  double rope_base, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The query side of one decode step: for each of `rows` query rows with
+ * hidden state x[r] and position pos[r], the query latent c_Q = W_DQ x
+ * (d_qc values), then per head i the content query q[r][i] = W_UQ[i] c_Q
+ * and the RoPE query q_r[r][i] = RoPE(W_QR[i] c_Q, pos[r]) (the query
+ * down-projection and per-head up-projections of "Multi-Head Latent
+ * Attention: ..."; "MLA, dim by dim" section 4.3, in the order
+ * (x W_DQ) W_UQ, and 5.2; "From Vanilla Transformers ..." sections 3.d and
+ * 3.l) -- the q and q_r that `run` takes.  Device memory in `dtype`:
+ *   x [rows][d_model]; w_dq [d_qc][d_model]; w_uq [h][d_h][d_qc];
+ *   w_qr [h][d_r][d_qc]; pos [rows] int32;
+ *   q [rows][h][d_h]; q_r [rows][h][d_r];
+ *   workspace mla_query_project_workspace_size bytes, 256-byte aligned
+ *   (c_Q, kept in dtype -- bf16 rounds it to nearest even as the next
+ *   product's operand -- and fp32 partial sums).
+ * RoPE as for mla_cache_append_run.  bf16 with d_model and d_qc multiples of
+ * 512 and d_qc, h * d_h, h * d_r multiples of 64 runs on MFMA; other shapes
+ * and fp32 on plain kernels.  Enqueued on `stream`; no allocation, no
+ * synchronisation; argument errors return a negative status before any
+ * launch. */
+size_t mla_query_project_workspace_size(int32_t rows, int32_t d_model, int32_t d_qc, int32_t h, int32_t d_h,
+                                        int32_t d_r, int32_t dtype);
+mla_status_t mla_query_project_run(int32_t rows, int32_t d_model, int32_t d_qc, int32_t h, int32_t d_h,
+                                   int32_t d_r, int32_t dtype, const void* x, const void* w_dq,
+                                   const void* w_uq, const void* w_qr, const int32_t* pos, void* q,
+                                   void* q_r, const double* rope_theta, double rope_base, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Releases a plan.  NULL is accepted and ignored. */
 void mla_decode_destroy(mla_decode_t plan);
 

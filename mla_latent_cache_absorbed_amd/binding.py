@@ -30,7 +30,9 @@ _DTYPE = {"bf16": MLA_DTYPE_BF16, "f32": MLA_DTYPE_F32}
 EXPORTED = ("mla_decode_create", "mla_decode_workspace_size", "mla_decode_split_plan",
             "mla_decode_run", "mla_decode_run_static", "mla_decode_enable_timing",
             "mla_decode_read_timing", "mla_decode_read_timing_runs", "mla_decode_destroy",
-            "mla_decode_last_error", "mla_oproj_workspace_size", "mla_oproj_run")
+            "mla_decode_last_error", "mla_oproj_workspace_size", "mla_oproj_run",
+            "mla_cache_append_workspace_size", "mla_cache_append_run",
+            "mla_query_project_workspace_size", "mla_query_project_run")
 
 KERNELS = ("q_absorb", "split_attn", "combine", "up_project")
 
@@ -87,6 +89,15 @@ def lib():
         L.mla_oproj_workspace_size.restype = sz
         L.mla_oproj_run.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.mla_oproj_run.restype = ctypes.c_int
+        dbl = ctypes.c_double
+        L.mla_cache_append_workspace_size.argtypes = [i32] * 5
+        L.mla_cache_append_workspace_size.restype = sz
+        L.mla_cache_append_run.argtypes = [i32] * 5 + [vp] * 6 + [i32] * 3 + [vp, vp, vp, dbl, vp, sz, vp]
+        L.mla_cache_append_run.restype = ctypes.c_int
+        L.mla_query_project_workspace_size.argtypes = [i32] * 7
+        L.mla_query_project_workspace_size.restype = sz
+        L.mla_query_project_run.argtypes = [i32] * 7 + [vp] * 8 + [dbl, vp, sz, vp]
+        L.mla_query_project_run.restype = ctypes.c_int
         L.mla_decode_destroy.argtypes = [vp]
         L.mla_decode_destroy.restype = None
         L.mla_decode_last_error.argtypes = []
@@ -254,6 +265,117 @@ class OutputProjection:
         ws = self.workspace(rows, o.device)
         return mla_oproj_run(rows, self.k, self.d, o, w_o, u, ws, dtype=self.dtype, out_dtype=self.out_dtype,
                              stream=stream)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def _nbytes(t):
+    return 0 if t is None or isinstance(t, int) else t.numel() * t.element_size()
+
+
+def mla_cache_append_workspace_size(rows, d_model, d_c, d_r, dtype="bf16") -> int:
+    return int(lib().mla_cache_append_workspace_size(rows, d_model, d_c, d_r, _DTYPE[dtype]))
+
+
+def mla_cache_append_run(rows, d_model, d_c, d_r, x, w_dkv, w_kr, seq, pos, page_table, max_pages_per_seq,
+                         page_size, num_pages, latent_pool, rope_pool, rope_theta=None, rope_base=10000.0,
+                         workspace=None, workspace_bytes=None, dtype="bf16", stream=None) -> int:
+    """Write c = W_DKV x and k_R = RoPE(W_KR x, pos) of each new token into
+    its pool rows (tensors or raw device addresses)."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    return _check(lib().mla_cache_append_run(
+        rows, d_model, d_c, d_r, _DTYPE[dtype], _ptr(x), _ptr(w_dkv), _ptr(w_kr), _ptr(seq), _ptr(pos),
+        _ptr(page_table), max_pages_per_seq, page_size, num_pages, _ptr(latent_pool), _ptr(rope_pool),
+        _ptr(rope_theta), float(rope_base), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mla_query_project_workspace_size(rows, d_model, d_qc, h, d_h, d_r, dtype="bf16") -> int:
+    return int(lib().mla_query_project_workspace_size(rows, d_model, d_qc, h, d_h, d_r, _DTYPE[dtype]))
+
+
+def mla_query_project_run(rows, d_model, d_qc, h, d_h, d_r, x, w_dq, w_uq, w_qr, pos, q, q_r, rope_theta=None,
+                          rope_base=10000.0, workspace=None, workspace_bytes=None, dtype="bf16",
+                          stream=None) -> int:
+    """q = W_UQ (W_DQ x) per head and q_R = RoPE(W_QR (W_DQ x), pos) of each
+    query row (tensors or raw device addresses)."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    return _check(lib().mla_query_project_run(
+        rows, d_model, d_qc, h, d_h, d_r, _DTYPE[dtype], _ptr(x), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(pos),
+        _ptr(q), _ptr(q_r), _ptr(rope_theta), float(rope_base), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def _device_workspace(nbytes, device):
+    import torch
+    return None if nbytes == 0 else torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+class CacheAppend:
+    """The cache append of a step on torch tensors (shape, dtype and
+    placement checks, a workspace, then mla_cache_append_run)."""
+
+    def __init__(self, d_model, d_c, d_r, dtype="bf16", rope_base=10000.0, rope_theta=None):
+        self.d_model, self.d_c, self.d_r, self.dtype = int(d_model), int(d_c), int(d_r), dtype
+        self.rope_base, self.rope_theta = float(rope_base), rope_theta
+
+    def run(self, x, w_dkv, w_kr, seq, pos, page_table, latent_pool, rope_pool, stream=None):
+        import torch
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+        rows = x.shape[0]
+        checks = (("x", x, (rows, self.d_model), dt), ("w_dkv", w_dkv, (self.d_c, self.d_model), dt),
+                  ("w_kr", w_kr, (self.d_r, self.d_model), dt), ("seq", seq, (rows,), torch.int32),
+                  ("pos", pos, (rows,), torch.int32), ("page_table", page_table, None, torch.int32),
+                  ("latent_pool", latent_pool, None, dt), ("rope_pool", rope_pool, None, dt))
+        for name, t, shape, want in checks:
+            if t.dtype != want or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous CUDA tensor of %s" % (name, want))
+            if shape is not None and tuple(t.shape) != shape:
+                raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        num_pages, page_size = latent_pool.shape[0], latent_pool.shape[1]
+        if tuple(latent_pool.shape) != (num_pages, page_size, self.d_c) or \
+                tuple(rope_pool.shape) != (num_pages, page_size, self.d_r) or page_table.dim() != 2:
+            raise ValueError("pools must be [num_pages][page_size][d_c | d_r] and page_table 2-D")
+        ws = _device_workspace(mla_cache_append_workspace_size(rows, self.d_model, self.d_c, self.d_r, self.dtype),
+                               x.device)
+        return mla_cache_append_run(rows, self.d_model, self.d_c, self.d_r, x, w_dkv, w_kr, seq, pos, page_table,
+                                    page_table.shape[1], page_size, num_pages, latent_pool, rope_pool,
+                                    self.rope_theta, self.rope_base, ws, dtype=self.dtype, stream=stream)
+
+
+class QueryProjection:
+    """The query side of a step on torch tensors (checks, a workspace, then
+    mla_query_project_run)."""
+
+    def __init__(self, d_model, d_qc, h, d_h, d_r, dtype="bf16", rope_base=10000.0, rope_theta=None):
+        self.d_model, self.d_qc, self.h, self.d_h, self.d_r = int(d_model), int(d_qc), int(h), int(d_h), int(d_r)
+        self.dtype, self.rope_base, self.rope_theta = dtype, float(rope_base), rope_theta
+
+    def run(self, x, w_dq, w_uq, w_qr, pos, q, q_r, stream=None):
+        import torch
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32}[self.dtype]
+        rows = x.shape[0]
+        checks = (("x", x, (rows, self.d_model), dt), ("w_dq", w_dq, (self.d_qc, self.d_model), dt),
+                  ("w_uq", w_uq, (self.h, self.d_h, self.d_qc), dt), ("w_qr", w_qr, (self.h, self.d_r, self.d_qc), dt),
+                  ("pos", pos, (rows,), torch.int32), ("q", q, None, dt), ("q_r", q_r, None, dt))
+        for name, t, shape, want in checks:
+            if t.dtype != want or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous CUDA tensor of %s" % (name, want))
+            if shape is not None and tuple(t.shape) != shape:
+                raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+        if q.numel() != rows * self.h * self.d_h or q_r.numel() != rows * self.h * self.d_r:
+            raise ValueError("q must hold rows x h x d_h and q_r rows x h x d_r values")
+        ws = _device_workspace(mla_query_project_workspace_size(rows, self.d_model, self.d_qc, self.h, self.d_h,
+                                                                self.d_r, self.dtype), x.device)
+        return mla_query_project_run(rows, self.d_model, self.d_qc, self.h, self.d_h, self.d_r, x, w_dq, w_uq, w_qr,
+                                     pos, q, q_r, self.rope_theta, self.rope_base, ws, dtype=self.dtype,
+                                     stream=stream)
 
 
 def mla_decode_destroy(plan) -> None:

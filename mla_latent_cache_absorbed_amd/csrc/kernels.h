@@ -102,5 +102,52 @@ int oproj_splits(int rows, int k, int d);
 // fp32 partial bytes the launch needs in OprojLaunch::part (0: none).
 size_t oproj_workspace_bytes(int rows, int k, int d, bool bf16);
 hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s);
+// The same MFMA product on x [rows][k] (bf16) and the stacked weights
+// [w0 ([d0][k]); w1 ([d - d0][k])], both bf16 with d0 and d multiples of 64
+// (and oproj_fast_applies(k, d, true)): writes the fp32 slice partials
+// [oproj_splits(rows, k, d)][rows][d] into part, for a caller's own finish.
+hipError_t launch_proj_partial(const void* x, const void* w0, const void* w1, int rows, int k, int d, int d0,
+                               float* part, const LaunchCtx& s);
+
+// The cache append of a step (rope_proj.hip): c = W_DKV x and
+// k_R = RoPE(W_KR x, pos) of each new token into its pool rows.
+struct AppendLaunch {
+  const void* x;      // [rows][d_model]
+  const void* w_dkv;  // [d_c][d_model]
+  const void* w_kr;   // [d_r][d_model]
+  int rows = 0, d_model = 0, d_c = 0, d_r = 0;
+  const int32_t* seq;         // [rows]
+  const int32_t* pos;         // [rows]
+  const int32_t* page_table;  // [batch][max_pages]
+  int max_pages = 0, page_size = 0, num_pages = 0;
+  void* latent_pool;  // [num_pages][page_size][d_c]
+  void* rope_pool;    // [num_pages][page_size][d_r]
+  const double* theta;  // [d_r / 2] RoPE frequencies, or null: base^(-2j/d_r)
+  double base = 10000.0;
+  bool bf16 = true;
+  void* work;  // cache_append_workspace_bytes
+};
+bool cache_append_fast(int d_model, int d_c, int d_r, bool bf16);
+size_t cache_append_workspace_bytes(int rows, int d_model, int d_c, int d_r, bool bf16);
+hipError_t launch_cache_append(const AppendLaunch& p, const LaunchCtx& s);
+
+// The query side of a step (rope_proj.hip): c_Q = W_DQ x, q_i = W_UQ[i] c_Q,
+// q_R,i = RoPE(W_QR[i] c_Q, pos).
+struct QueryLaunch {
+  const void* x;     // [rows][d_model]
+  const void* w_dq;  // [d_qc][d_model]
+  const void* w_uq;  // [h d_h][d_qc]
+  const void* w_qr;  // [h d_r][d_qc]
+  int rows = 0, d_model = 0, d_qc = 0, h = 0, d_h = 0, d_r = 0;
+  const int32_t* pos;  // [rows]
+  void* q;             // [rows][h][d_h]
+  void* q_r;           // [rows][h][d_r]
+  const double* theta;
+  double base = 10000.0;
+  bool bf16 = true;
+  void* work;  // query_project_workspace_bytes: c_Q, then the fp32 partials
+};
+size_t query_project_workspace_bytes(int rows, int d_model, int d_qc, int h, int d_h, int d_r, bool bf16);
+hipError_t launch_query_project(const QueryLaunch& p, const LaunchCtx& s);
 
 }  // namespace mla

@@ -47,11 +47,12 @@ constexpr int kRowsPerGroup = 64;
 constexpr int kDepth = 4;      // k-steps of loads in flight per wave
 
 struct OprojArgs {
-  const uint16_t* o;  // [rows][k]
-  const uint16_t* w;  // [d][k]
-  float* part;        // [splits][rows][d] (splits > 1)
-  void* u;            // [rows][d]
-  int rows, k, d, splits, out_bf16;
+  const uint16_t* o;   // [rows][k]
+  const uint16_t* w;   // [d0][k]: output features 0 .. d0 - 1
+  const uint16_t* w1;  // [d - d0][k]: output features d0 .. d - 1 (a second stacked weight)
+  float* part;         // [splits][rows][d] (splits > 1, or always with write_part)
+  void* u;             // [rows][d]
+  int rows, k, d, d0, splits, out_bf16, write_part;
 };
 
 template <int kRb>  // 16-row blocks per work-group (1, 2 or 4)
@@ -68,7 +69,9 @@ __global__ __launch_bounds__(kThreads) void oproj_partial_kernel(OprojArgs a) {
   const int k0 = (slice * kWaves + wave) * kw;
 
   // A operand of feature block j, k-step s: W[n0 + 16 j + l16][k0 + 32 s + 8 g .. + 7]
-  const uint16_t* wp = a.w + (size_t)(n0 + l16) * a.k + k0 + 8 * g;
+  // (a work-group's 64 features lie in one of the two stacked weights)
+  const uint16_t* wp = n0 < a.d0 ? a.w + (size_t)(n0 + l16) * a.k + k0 + 8 * g
+                                 : a.w1 + (size_t)(n0 - a.d0 + l16) * a.k + k0 + 8 * g;
   const size_t wj = (size_t)16 * a.k;  // next feature block
   // B operand of row block rb: o[r0 + 16 rb + l16][k0 + 32 s + 8 g .. + 7]; a
   // row past the end reads row r0 instead (its results are never stored)
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void oproj_partial_kernel(OprojArgs a) {
     const int row = r0 + 16 * rb + l16;
     if (row >= a.rows) continue;
     const size_t idx = (size_t)row * a.d + n;
-    if (a.splits > 1) {
+    if (a.splits > 1 || a.write_part) {
       *reinterpret_cast<f32x4*>(a.part + (size_t)slice * a.rows * a.d + idx) = v;
     } else if (a.out_bf16) {
       *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.u) + idx) = u32x2{pack_bf16x2(v[0], v[1]),
@@ -168,19 +171,51 @@ __global__ __launch_bounds__(kThreads) void oproj_general_kernel(const Tin* o, c
   store_from_f32(u, i, acc);
 }
 
+int splits_for(int rows, int k, int d) {
+  const int groups = (d / kFeatures) * ((rows + kRowsPerGroup - 1) / kRowsPerGroup);
+  // The smallest slice count that gives at least 1024 work-groups (16 slices
+  // at k = 16384, d = 5120: 1, 32 and 64 rows ran 2-8 % faster than with 8
+  // slices, and 32 slices slower again), else the most there can be; every
+  // wave keeps whole unrolled k-steps, so the count divides k / 512.
+  const int units = k / (kWaves * 32 * kDepth);
+  for (int s = 1; s <= units; ++s)
+    if (units % s == 0 && groups * s >= 1024) return s;
+  return units;
+}
+
+// The MFMA partial kernel on x [rows][k] times the stacked weights [w0
+// ([d0][k]); w1 ([d - d0][k])]^T; `used` receives the arguments it ran with.
+hipError_t launch_partial(const void* x, const void* w0, const void* w1, int rows, int k, int d, int d0,
+                                 float* part, bool write_part, void* u, bool out_bf16, const LaunchCtx& s,
+                                 OprojArgs* used) {
+  OprojArgs a;
+  a.o = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(w0);
+  a.w1 = static_cast<const uint16_t*>(w1);
+  a.part = part;
+  a.u = u;
+  a.rows = rows;
+  a.k = k;
+  a.d = d;
+  a.d0 = d0;
+  a.splits = splits_for(rows, k, d);
+  a.out_bf16 = out_bf16;
+  a.write_part = write_part;
+  const dim3 grid(d / kFeatures, a.splits, (rows + kRowsPerGroup - 1) / kRowsPerGroup);
+  if (rows <= 16)
+    launch_kernel(oproj_partial_kernel<1>, grid, dim3(kThreads), s, a);
+  else if (rows <= 32)
+    launch_kernel(oproj_partial_kernel<2>, grid, dim3(kThreads), s, a);
+  else
+    launch_kernel(oproj_partial_kernel<4>, grid, dim3(kThreads), s, a);
+  if (used) *used = a;
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool oproj_fast_applies(int k, int d, bool bf16) { return bf16 && d % kFeatures == 0 && k % (kWaves * 32 * kDepth) == 0; }
 
-int oproj_splits(int rows, int k, int d) {
-  const int groups = (d / kFeatures) * ((rows + kRowsPerGroup - 1) / kRowsPerGroup);
-  int s = 1;
-  // at least 1024 work-groups (16 slices at d = 5120: 1, 32 and 64 rows ran
-  // 2-8 % faster than with 8 slices, and 32 slices slower again), each wave
-  // keeping whole unrolled k-steps
-  while (groups * s < 1024 && k % (2 * s * kWaves * 32 * kDepth) == 0) s *= 2;
-  return s;
-}
 
 hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s) {
   if (p.rows == 0) return hipSuccess;
@@ -204,27 +239,21 @@ hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s) {
     return hipGetLastError();
   }
   OprojArgs a;
-  a.o = static_cast<const uint16_t*>(p.o);
-  a.w = static_cast<const uint16_t*>(p.w);
-  a.part = static_cast<float*>(p.part);
-  a.u = p.u;
-  a.rows = p.rows;
-  a.k = p.k;
-  a.d = p.d;
-  a.splits = oproj_splits(p.rows, p.k, p.d);
-  a.out_bf16 = p.out_bf16;
-  const dim3 grid(p.d / kFeatures, a.splits, (p.rows + kRowsPerGroup - 1) / kRowsPerGroup);
-  if (p.rows <= 16)
-    launch_kernel(oproj_partial_kernel<1>, grid, dim3(kThreads), s, a);
-  else if (p.rows <= 32)
-    launch_kernel(oproj_partial_kernel<2>, grid, dim3(kThreads), s, a);
-  else
-    launch_kernel(oproj_partial_kernel<4>, grid, dim3(kThreads), s, a);
+  const hipError_t e = launch_partial(p.o, p.w, nullptr, p.rows, p.k, p.d, p.d, static_cast<float*>(p.part), false,
+                                      p.u, p.out_bf16, s, &a);
+  if (e != hipSuccess) return e;
   if (a.splits > 1) {
     const size_t total4 = (size_t)p.rows * p.d / 4;
     launch_kernel(oproj_reduce_kernel, dim3((unsigned)((total4 + kThreads - 1) / kThreads)), dim3(kThreads), s, a);
   }
   return hipGetLastError();
+}
+
+int oproj_splits(int rows, int k, int d) { return splits_for(rows, k, d); }
+
+hipError_t launch_proj_partial(const void* x, const void* w0, const void* w1, int rows, int k, int d, int d0,
+                               float* part, const LaunchCtx& s) {
+  return launch_partial(x, w0, w1, rows, k, d, d0, part, true, nullptr, false, s, nullptr);
 }
 
 size_t oproj_workspace_bytes(int rows, int k, int d, bool bf16) {

@@ -239,3 +239,31 @@ def make_oproj(rows: int, h: int = 128, d_h: int = 128, d_model: int = D_MODEL, 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
     """bf16 patterns or fp32 values -> float64 (exact)."""
     return bf16_to_f32(a).astype(np.float64) if dtype == "bf16" else np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# The current token's projections (cache append and query side)
+# --------------------------------------------------------------------------
+# DeepSeek-V2's query latent width d_c' ("MLA Explained", section "Query
+# compression: an optional bonus").
+D_QC = 1536
+
+
+def make_projections(rows: int, d_model: int = D_MODEL, d_c: int = 512, d_r: int = 64, d_qc: int = D_QC,
+                     h: int = 128, d_h: int = 128, dtype: str = "bf16", seed: int = 400) -> dict:
+    """Hidden states x [rows][d_model] ~ N(0, 1), then W_DKV [d_c][d_model],
+    W_KR [d_r][d_model], W_DQ [d_qc][d_model] ~ N(0, 1/d_model) and
+    W_UQ [h][d_h][d_qc], W_QR [h][d_r][d_qc] ~ N(0, 1/d_qc) (variance
+    1/fan-in), drawn in that order, bf16 patterns or float32."""
+    rng = np.random.default_rng(seed)
+
+    def draw(shape, fan_in):
+        a = rng.standard_normal(shape, dtype=np.float32)
+        return a if fan_in is None else (a / np.float32(np.sqrt(fan_in))).astype(np.float32)
+
+    out = dict(x=draw((rows, d_model), None), w_dkv=draw((d_c, d_model), d_model), w_kr=draw((d_r, d_model), d_model),
+               w_dq=draw((d_qc, d_model), d_model), w_uq=draw((h, d_h, d_qc), d_qc), w_qr=draw((h, d_r, d_qc), d_qc))
+    if dtype == "bf16":
+        out = {k: bf16_bits(v) for k, v in out.items()}
+    out.update(dtype=dtype, rows=rows, d_model=d_model, d_c=d_c, d_r=d_r, d_qc=d_qc, h=h, d_h=d_h)
+    return out

@@ -23,7 +23,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj|cache_append|query_project)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -201,3 +201,31 @@ def test_output_projection_refuses_bad_calls_on_the_host(L):
     assert e.value.status == binding.MLA_ERR_WORKSPACE
     assert "327680 needed" in binding.mla_decode_last_error()
     assert binding.mla_oproj_run(0, 16384, 5120, None, None, None, stream=0) == binding.MLA_OK  # nothing to do
+
+
+def test_projections_refuse_bad_calls_on_the_host(L):
+    # cache append: 9 MFMA blocks of 64 features, k = 5120 in 10 slices
+    assert binding.mla_cache_append_workspace_size(1, 5120, 512, 64) == 10 * 576 * 4
+    assert binding.mla_cache_append_workspace_size(4, 5, 2, 2, "f32") == 0
+    assert binding.mla_cache_append_workspace_size(1, 5120, 512, 63) == 0  # odd d_r
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_cache_append_run(1, 5120, 512, 63, *([None] * 6), 4, 64, 8, None, None, stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    with pytest.raises(binding.MLAError) as e:  # NULL tensors
+        binding.mla_cache_append_run(1, 5120, 512, 64, *([None] * 6), 4, 64, 8, None, None, stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    with pytest.raises(binding.MLAError) as e:  # no workspace
+        binding.mla_cache_append_run(1, 5120, 512, 64, *([4096] * 6), 4, 64, 8, 4096, 4096, stream=0)
+    assert e.value.status == binding.MLA_ERR_WORKSPACE
+    with pytest.raises(binding.MLAError) as e:  # no frequencies and a base <= 1
+        binding.mla_cache_append_run(1, 5120, 512, 64, *([4096] * 6), 4, 64, 8, 4096, 4096, rope_base=1.0,
+                                     stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    # query side: c_Q (256-aligned) plus the larger of the two stages' partials
+    need = binding.mla_query_project_workspace_size(1, 5120, 1536, 128, 128, 64)
+    assert need == 3072 + max(10 * 1536 * 4, 3 * 128 * 192 * 4)
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_query_project_run(1, 5120, 1536, 128, 128, 64, *([4096] * 7), workspace=4096,
+                                      workspace_bytes=need - 1, stream=0)
+    assert e.value.status == binding.MLA_ERR_WORKSPACE
+    assert binding.mla_query_project_run(0, 5120, 1536, 128, 128, 64, *([None] * 7), stream=0) == binding.MLA_OK

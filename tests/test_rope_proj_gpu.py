@@ -1,0 +1,217 @@
+"""GPU parity of the current token's projections (the steps before the
+decode path) through the C ABI, against the fp64 oracle on the same seeded
+inputs: the cache append (latent and rotated RoPE key into the paged pools)
+and the query side (query latent, content query, RoPE query).
+
+- The pages' toy on the plain fp32 kernels, against its printed values.
+- DeepSeek-V2 widths (d_model 5120, d_c 512, d_r 64, d_qc 1536, 128 heads of
+  128) on the MFMA path, with positions up to 131071 (fp64 angles).
+- One whole step from hidden states: cache append, query side, decode and
+  output projection on the GPU against the same chain in the oracle.
+
+Tolerance (normwise): 1e-2 for bf16 outputs, 1e-5 for fp32."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from mla_latent_cache_absorbed_amd import binding, inputs
+from tests._parity import check, log
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PJ = json.load(open(os.path.join(ROOT, "tests", "golden", "p5_toy_projections.json")))
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+def _v(key):
+    return np.asarray(PJ[key]["value"], dtype=np.float64)
+
+
+def _dev(torch, a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def _heads_of(m):
+    m = np.asarray(m, dtype=np.float64)
+    return np.stack([m[:, 2 * i:2 * i + 2].T for i in range(m.shape[1] // 2)])
+
+
+def test_p5_toy_cache_append(torch):
+    """Sections 3.b and 3.k through the plain fp32 kernel: four tokens, one
+    per page, shuffled pages, 90 degrees per position."""
+    table = np.array([[2, 0, 3, 1]], np.int32)
+    lat = torch.full((4, 1, 2), float("nan"), device="cuda")
+    rp = torch.full((4, 1, 2), float("nan"), device="cuda")
+    theta = torch.tensor([math.pi / 2], dtype=torch.float64, device="cuda")
+    op = binding.CacheAppend(5, 2, 2, "f32", rope_theta=theta)
+    op.run(_dev(torch, _v("hidden"), "f32"), _dev(torch, _v("W_DKV").T, "f32"), _dev(torch, _v("W_KR").T, "f32"),
+           torch.zeros(4, dtype=torch.int32, device="cuda"), torch.arange(4, dtype=torch.int32, device="cuda"),
+           torch.from_numpy(table).cuda(), lat, rp)
+    torch.cuda.synchronize()
+    for t in range(4):
+        np.testing.assert_allclose(lat[table[0, t], 0].cpu().numpy(), _v("latents")[t], rtol=0, atol=1e-6)
+        np.testing.assert_allclose(rp[table[0, t], 0].cpu().numpy(), _v("rope_keys_rotated")[t], rtol=0, atol=1e-6)
+
+
+def test_p5_toy_query_side(torch):
+    """Sections 3.d and 3.l through the plain fp32 kernels (the toy's query
+    latent is the hidden state: W_DQ = identity)."""
+    theta = torch.tensor([math.pi / 2], dtype=torch.float64, device="cuda")
+    q = torch.full((1, 2, 2), float("nan"), device="cuda")
+    q_r = torch.full((1, 2, 2), float("nan"), device="cuda")
+    op = binding.QueryProjection(5, 5, 2, 2, 2, "f32", rope_theta=theta)
+    op.run(_dev(torch, _v("hidden")[3:4], "f32"), _dev(torch, np.eye(5), "f32"),
+           _dev(torch, _heads_of(PJ["W_Q"]["value"]), "f32"), _dev(torch, _heads_of(PJ["W_QR"]["value"]), "f32"),
+           torch.tensor([3], dtype=torch.int32, device="cuda"), q, q_r)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(q[0].cpu().numpy(), _v("q"), rtol=0, atol=1e-6)
+    np.testing.assert_allclose(q_r[0].cpu().numpy(), _v("q_rope_rotated"), rtol=0, atol=1e-6)
+
+
+def _paged_layout(rng, seqs, max_pages, page_size):
+    """A shuffled page table for `seqs` sequences of max_pages pages each."""
+    num_pages = seqs * max_pages
+    return rng.permutation(num_pages).reshape(seqs, max_pages).astype(np.int32), num_pages
+
+
+@pytest.mark.parametrize("rows", [1, 32, 64])
+def test_cache_append_deepseek_v2(torch, rows):
+    rng = np.random.default_rng(410 + rows)
+    case = inputs.make_projections(rows, seed=420 + rows)
+    seqs, page_size = 4, 64
+    max_pages = 131072 // page_size
+    table, num_pages = _paged_layout(rng, seqs, max_pages, page_size)
+    seq = rng.integers(0, seqs, size=rows).astype(np.int32)
+    pos = rng.choice(131072, size=rows, replace=False).astype(np.int32)  # distinct rows, positions up to 2^17 - 1
+    pos[0] = 131071
+    lat = torch.zeros((num_pages, page_size, 512), dtype=torch.bfloat16, device="cuda")
+    rp = torch.zeros((num_pages, page_size, 64), dtype=torch.bfloat16, device="cuda")
+    op = binding.CacheAppend(5120, 512, 64, "bf16")
+    op.run(_dev(torch, case["x"], "bf16"), _dev(torch, case["w_dkv"], "bf16"), _dev(torch, case["w_kr"], "bf16"),
+           torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(table).cuda(), lat, rp)
+    torch.cuda.synchronize()
+    w = {k: inputs.widen(case[k], "bf16") for k in ("x", "w_dkv", "w_kr")}
+    th = oracle.rope_thetas(64, 10000.0)
+    # the oracle writes into compact pools holding only the touched pages
+    pages = table[seq, pos // page_size]
+    used = np.unique(pages)
+    compact = np.full(table.shape, -1, np.int32)
+    for b_, row in enumerate(table):
+        for j, pg in enumerate(row):
+            hit = np.searchsorted(used, pg)
+            if hit < used.size and used[hit] == pg:
+                compact[b_, j] = hit
+    ref_lat, ref_rp = oracle.cache_append(w["x"], w["w_dkv"], w["w_kr"], seq, pos, th, compact, page_size,
+                                          np.zeros((used.size, page_size, 512)), np.zeros((used.size, page_size, 64)))
+    ci = np.searchsorted(used, pages).astype(np.int64) * page_size + pos % page_size
+    gi = torch.from_numpy(pages.astype(np.int64) * page_size + pos % page_size).cuda()
+    lat_h = lat.view(-1, 512)[gi].float().cpu().numpy().astype(np.float64)
+    rp_h = rp.view(-1, 64)[gi].float().cpu().numpy().astype(np.float64)
+    check(lat_h, ref_lat.reshape(-1, 512)[ci], "bf16", "cache append latent rows=%d" % rows)
+    check(rp_h, ref_rp.reshape(-1, 64)[ci], "bf16", "cache append RoPE key rows=%d (positions up to %d)"
+          % (rows, pos.max()))
+    # nothing else was written
+    assert int((lat.view(-1, 512).abs().sum(1) != 0).sum()) == rows
+    assert int((rp.view(-1, 64).abs().sum(1) != 0).sum()) == rows
+
+
+def test_cache_append_skips_rows_outside_the_table(torch):
+    """A position past the table, or a page id outside the pool, writes
+    nothing (the other rows are still written)."""
+    case = inputs.make_projections(3, seed=430)
+    table = np.array([[0, 1], [2, 99]], np.int32)  # sequence 1's second page is not in the 3-page pool
+    seq = np.array([0, 0, 1], np.int32)
+    pos = np.array([5, 128, 70], np.int32)         # row 1: past the table; row 2: page 99
+    lat = torch.zeros((3, 64, 512), dtype=torch.bfloat16, device="cuda")
+    rp = torch.zeros((3, 64, 64), dtype=torch.bfloat16, device="cuda")
+    binding.CacheAppend(5120, 512, 64, "bf16").run(
+        _dev(torch, case["x"], "bf16"), _dev(torch, case["w_dkv"], "bf16"), _dev(torch, case["w_kr"], "bf16"),
+        torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(table).cuda(), lat, rp)
+    torch.cuda.synchronize()
+    written = (lat.view(-1, 512).abs().sum(1) != 0).nonzero().flatten().tolist()
+    assert written == [5]  # page 0, row 5
+    assert (rp.view(-1, 64).abs().sum(1) != 0).nonzero().flatten().tolist() == [5]
+
+
+@pytest.mark.parametrize("rows", [1, 16, 64])
+def test_query_side_deepseek_v2(torch, rows):
+    case = inputs.make_projections(rows, seed=440 + rows)
+    pos = np.random.default_rng(450 + rows).integers(0, 131072, size=rows).astype(np.int32)
+    pos[0] = 131071
+    q = torch.full((rows, 128, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    q_r = torch.full((rows, 128, 64), float("nan"), dtype=torch.bfloat16, device="cuda")
+    binding.QueryProjection(5120, 1536, 128, 128, 64, "bf16").run(
+        *(_dev(torch, case[k], "bf16") for k in ("x", "w_dq", "w_uq", "w_qr")), torch.from_numpy(pos).cuda(), q, q_r)
+    torch.cuda.synchronize()
+    w = {k: inputs.widen(case[k], "bf16") for k in ("x", "w_dq", "w_uq", "w_qr")}
+    ref_q, ref_qr = oracle.query_project(w["x"], w["w_dq"], w["w_uq"], w["w_qr"], pos, oracle.rope_thetas(64, 10000.0))
+    check(q.float().cpu().numpy().astype(np.float64), ref_q, "bf16", "query side q rows=%d" % rows)
+    check(q_r.float().cpu().numpy().astype(np.float64), ref_qr, "bf16", "query side q_R rows=%d" % rows)
+
+
+def test_query_side_odd_shape_plain_kernels(torch):
+    """bf16 storage off the MFMA shapes (plain kernels for both stages)."""
+    case = inputs.make_projections(5, d_model=300, d_c=16, d_r=6, d_qc=70, h=3, d_h=10, seed=460)
+    pos = np.array([0, 1, 17, 4000, 99999], np.int32)
+    q = torch.empty((5, 3, 10), dtype=torch.bfloat16, device="cuda")
+    q_r = torch.empty((5, 3, 6), dtype=torch.bfloat16, device="cuda")
+    binding.QueryProjection(300, 70, 3, 10, 6, "bf16").run(
+        *(_dev(torch, case[k], "bf16") for k in ("x", "w_dq", "w_uq", "w_qr")), torch.from_numpy(pos).cuda(), q, q_r)
+    torch.cuda.synchronize()
+    w = {k: inputs.widen(case[k], "bf16") for k in ("x", "w_dq", "w_uq", "w_qr")}
+    # the GPU rounds c_Q to bf16 between the two products (its storage type):
+    # the oracle gets the same rounding by running its second stage on it
+    cq = inputs.widen(inputs.bf16_bits((w["w_dq"] @ w["x"].T).T.astype(np.float32)), "bf16")
+    ref_q, ref_qr = oracle.query_project(cq, np.eye(70), w["w_uq"], w["w_qr"], pos, oracle.rope_thetas(6, 10000.0))
+    check(q.float().cpu().numpy().astype(np.float64), ref_q, "bf16", "query side q, plain kernels")
+    check(q_r.float().cpu().numpy().astype(np.float64), ref_qr, "bf16", "query side q_R, plain kernels")
+
+
+def test_one_step_from_hidden_states(torch):
+    """Cache append of each sequence's new token, the query side, the decode
+    step and the output projection on the GPU, against the same chain in
+    the oracle: two sequences whose earlier cache rows are random."""
+    from mla_latent_cache_absorbed_amd.runner import DeviceWorkload
+    wl = inputs.make("ds2_paged_b32", batch=2, lens=("list", [1500, 333]), seed=470)
+    lens = wl.lens.astype(np.int32)
+    case = inputs.make_projections(2, seed=471)  # one new token per sequence, at position L - 1
+    pos = lens - 1
+    seq = np.arange(2, dtype=np.int32)
+    dw = DeviceWorkload(wl)
+    dev = {k: _dev(torch, case[k], "bf16") for k in ("x", "w_dkv", "w_kr", "w_dq", "w_uq", "w_qr")}
+    binding.CacheAppend(5120, 512, 64, "bf16").run(dev["x"], dev["w_dkv"], dev["w_kr"], torch.from_numpy(seq).cuda(),
+                                                   torch.from_numpy(pos).cuda(), dw.t["page_table"],
+                                                   dw.t["latent_pool"], dw.t["rope_pool"])
+    q = torch.empty((2, 1, 128, 128), dtype=torch.bfloat16, device="cuda")
+    q_r = torch.empty((2, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
+    binding.QueryProjection(5120, 1536, 128, 128, 64, "bf16").run(dev["x"], dev["w_dq"], dev["w_uq"], dev["w_qr"],
+                                                                  torch.from_numpy(pos).cuda(), q, q_r)
+    dw.run(q=q, q_r=q_r)
+    w_o = inputs.make_oproj(1, seed=472)["w_o"]  # W^O in the pages' orientation
+    u = torch.empty((2, 5120), dtype=torch.float32, device="cuda")
+    binding.OutputProjection(16384, 5120, "bf16", "f32").run(
+        dw.out, torch.from_numpy(np.ascontiguousarray(w_o.T).view(np.int16)).view(torch.bfloat16).cuda(), u)
+    torch.cuda.synchronize()
+    # the oracle's chain on the same inputs
+    w = {k: inputs.widen(case[k], "bf16") for k in ("x", "w_dkv", "w_kr", "w_dq", "w_uq", "w_qr")}
+    th = oracle.rope_thetas(64, 10000.0)
+    lat, rp = oracle.cache_append(w["x"], w["w_dkv"], w["w_kr"], seq, pos, th, wl.page_table, wl.page_size,
+                                  inputs.as_f64(wl, "latent_pool"), inputs.as_f64(wl, "rope_pool"))
+    oq, oqr = oracle.query_project(w["x"], w["w_dq"], w["w_uq"], w["w_qr"], pos, th)
+    kw = inputs.oracle_problem_kwargs(wl)
+    kw.update(q=oq[:, None], q_r=oqr[:, None], latent_pool=lat, rope_pool=rp)
+    prob = oracle.Problem(**kw)
+    ref_u = oracle.output_project(oracle.decode_absorbed(prob), inputs.widen(w_o, "bf16")).reshape(2, -1)
+    check(u.cpu().numpy().astype(np.float64), ref_u, "bf16", "hidden states -> u, GPU chain vs oracle chain")

@@ -358,6 +358,24 @@ def decode_absorbed(prob: Problem, pairs=None, return_cbar: bool = False):
     return (out, cb) if return_cbar else out
 
 
+def prefill(latent, rope, q, q_r, w_uk, w_uv, scale=None, heads=None) -> np.ndarray:
+    """Causal attention over a prompt of T tokens in the explicit form (keys
+    and values rebuilt per head): the explicit decode with all T tokens as
+    new query tokens (query t sees tokens 0 .. t).  latent [T][d_c], rope
+    [T][d_r], q [T][h][d_h], q_r [T][h][d_r]; returns [T][h][d_h], or
+    [T][len(heads)][d_h] for the listed heads."""
+    latent = _f64(latent); rope = _f64(rope); q = _f64(q); q_r = _f64(q_r)
+    T, h, d_h = q.shape
+    d_r = q_r.shape[2]
+    prob = Problem(q=q[None], q_r=q_r[None], latent_pool=latent[None], rope_pool=rope[None],
+                   page_table=np.zeros((1, 1), np.int32), context_lens=np.array([T], np.int32),
+                   w_uk=w_uk, w_uv=w_uv, scale=(1.0 / np.sqrt(d_h + d_r)) if scale is None else scale)
+    if heads is None:
+        return decode_explicit(prob)[0]
+    out = decode_explicit(prob, [(0, int(i)) for i in heads])  # [len(heads)][T][d_h]
+    return np.ascontiguousarray(out.transpose(1, 0, 2))
+
+
 def gather(prob: Problem, b: int, n: int):
     """Logical cache rows of sequence b: (C [n, d_c], KR [n, d_r])."""
     S = prob._struct()

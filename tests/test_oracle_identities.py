@@ -314,3 +314,32 @@ def test_query_side_matches_matrix_products():
         for i in range(h):
             np.testing.assert_allclose(q[r, i], Wu[i] @ cq, rtol=1e-12, atol=1e-12)
             np.testing.assert_allclose(q_r[r, i], oracle.rope(Wr[i] @ cq, pos[r], th), rtol=1e-12, atol=1e-12)
+
+
+
+# --------------------------------------------------------------------------
+# Prefill: the explicit form with every prompt token as a query
+# --------------------------------------------------------------------------
+def test_prefill_is_causal_attention_over_rebuilt_keys_and_values():
+    """A special case that reduces to a library routine: per head, causal
+    scaled-dot-product attention (torch, float64, CPU) over keys
+    [W_UK[i] c_t; k_R,t] and values W_UV[i] c_t equals the oracle's prefill
+    ("MLA, dim by dim" section 4.1, the rebuilt K and V of prefill)."""
+    import torch
+    rng = np.random.default_rng(51)
+    T, h, d_c, d_r, d_h = 23, 3, 12, 4, 6
+    lat = rng.standard_normal((T, d_c)); rope = rng.standard_normal((T, d_r))
+    q = rng.standard_normal((T, h, d_h)); q_r = rng.standard_normal((T, h, d_r))
+    w_uk = rng.standard_normal((h, d_h, d_c)) / math.sqrt(d_c); w_uv = rng.standard_normal((h, d_h, d_c)) / math.sqrt(d_c)
+    got = oracle.prefill(lat, rope, q, q_r, w_uk, w_uv)
+    for i in range(h):
+        K = np.concatenate([lat @ w_uk[i].T, rope], axis=1)
+        V = lat @ w_uv[i].T
+        Q = np.concatenate([q[:, i], q_r[:, i]], axis=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None], is_causal=True,
+            scale=1.0 / math.sqrt(d_h + d_r))[0].numpy()
+        np.testing.assert_allclose(got[:, i], ref, rtol=1e-11, atol=1e-12)
+    # listed heads only
+    np.testing.assert_allclose(oracle.prefill(lat, rope, q, q_r, w_uk, w_uv, heads=[2, 0]), got[:, [2, 0]],
+                               rtol=0, atol=0)

@@ -286,6 +286,29 @@ mla_status_t mla_query_project_run(int32_t rows, int32_t d_model, int32_t d_qc, 
                                    void* q_r, const double* rope_theta, double rope_base, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Prefill: attention over a whole prompt of T tokens, each attending to
+ * itself and the tokens before it, in the order the pages derive for many
+ * queries ("MLA, dim by dim" section 4.1): the per-head keys and values are
+ * rebuilt from the latents, k_t,i = W_UK[i] c_t and v_t,i = W_UV[i] c_t,
+ * and the scores contract over d_h + d_r dimensions,
+ * s(t, u) = scale [q_t,i; q_R,t,i] . [k_u,i; k_R,u] for u <= t, then
+ * o_t,i = sum_u softmax(s) v_u,i (section 5.1 of the same page for the
+ * decoupled RoPE part).  scale 0 = 1 / sqrt(d_h + d_r).  Device memory in
+ * `dtype` (out in out_dtype, -1 = dtype):
+ *   latent [T][d_c]; rope [T][d_r] (already rotated); q [T][h][d_h];
+ *   q_r [T][h][d_r]; w_uk, w_uv [h][d_h][d_c]; out [T][h][d_h];
+ *   workspace mla_prefill_workspace_size bytes, 256-byte aligned (the
+ *   rebuilt K and V, [T][h][d_h] each, in dtype).
+ * bf16 with d_h = 128, d_r = 64 and d_c % 64 == 0 runs on MFMA (16-byte
+ * aligned tensors); other shapes and fp32 on plain kernels (meant for small
+ * problems).  Enqueued on `stream`; no allocation, no synchronisation;
+ * argument errors return a negative status before any launch. */
+size_t mla_prefill_workspace_size(int32_t T, int32_t h, int32_t d_h, int32_t dtype);
+mla_status_t mla_prefill_run(int32_t T, int32_t h, int32_t d_c, int32_t d_r, int32_t d_h, int32_t dtype,
+                             int32_t out_dtype, float scale, const void* latent, const void* rope,
+                             const void* q, const void* q_r, const void* w_uk, const void* w_uv, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Releases a plan.  NULL is accepted and ignored. */
 void mla_decode_destroy(mla_decode_t plan);
 

@@ -32,7 +32,8 @@ EXPORTED = ("mla_decode_create", "mla_decode_workspace_size", "mla_decode_split_
             "mla_decode_read_timing", "mla_decode_read_timing_runs", "mla_decode_destroy",
             "mla_decode_last_error", "mla_oproj_workspace_size", "mla_oproj_run",
             "mla_cache_append_workspace_size", "mla_cache_append_run",
-            "mla_query_project_workspace_size", "mla_query_project_run")
+            "mla_query_project_workspace_size", "mla_query_project_run",
+            "mla_prefill_workspace_size", "mla_prefill_run")
 
 KERNELS = ("q_absorb", "split_attn", "combine", "up_project")
 
@@ -98,6 +99,10 @@ def lib():
         L.mla_query_project_workspace_size.restype = sz
         L.mla_query_project_run.argtypes = [i32] * 7 + [vp] * 8 + [dbl, vp, sz, vp]
         L.mla_query_project_run.restype = ctypes.c_int
+        L.mla_prefill_workspace_size.argtypes = [i32] * 4
+        L.mla_prefill_workspace_size.restype = sz
+        L.mla_prefill_run.argtypes = [i32] * 7 + [ctypes.c_float] + [vp] * 8 + [sz, vp]
+        L.mla_prefill_run.restype = ctypes.c_int
         L.mla_decode_destroy.argtypes = [vp]
         L.mla_decode_destroy.restype = None
         L.mla_decode_last_error.argtypes = []
@@ -376,6 +381,50 @@ class QueryProjection:
         return mla_query_project_run(rows, self.d_model, self.d_qc, self.h, self.d_h, self.d_r, x, w_dq, w_uq, w_qr,
                                      pos, q, q_r, self.rope_theta, self.rope_base, ws, dtype=self.dtype,
                                      stream=stream)
+
+
+def mla_prefill_workspace_size(T, h, d_h, dtype="bf16") -> int:
+    return int(lib().mla_prefill_workspace_size(T, h, d_h, _DTYPE[dtype]))
+
+
+def mla_prefill_run(T, h, d_c, d_r, d_h, latent, rope, q, q_r, w_uk, w_uv, out, workspace, workspace_bytes=None,
+                    dtype="bf16", out_dtype=None, scale=0.0, stream=None) -> int:
+    """Causal attention over a prompt of T tokens with K and V rebuilt from
+    the latents (tensors or raw device addresses)."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    return _check(lib().mla_prefill_run(T, h, d_c, d_r, d_h, _DTYPE[dtype],
+                                        -1 if out_dtype is None else _DTYPE[out_dtype], float(scale), _ptr(latent),
+                                        _ptr(rope), _ptr(q), _ptr(q_r), _ptr(w_uk), _ptr(w_uv), _ptr(out),
+                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+class Prefill:
+    """Prefill attention on torch tensors (checks, a workspace, then
+    mla_prefill_run)."""
+
+    def __init__(self, h, d_c, d_r, d_h, dtype="bf16", out_dtype=None, scale=0.0):
+        self.h, self.d_c, self.d_r, self.d_h = int(h), int(d_c), int(d_r), int(d_h)
+        self.dtype, self.out_dtype, self.scale = dtype, out_dtype or dtype, float(scale)
+        self._ws = None
+
+    def run(self, latent, rope, q, q_r, w_uk, w_uv, out, stream=None):
+        import torch
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32}
+        T = latent.shape[0]
+        checks = (("latent", latent, (T, self.d_c), dt[self.dtype]), ("rope", rope, (T, self.d_r), dt[self.dtype]),
+                  ("q", q, (T, self.h, self.d_h), dt[self.dtype]), ("q_r", q_r, (T, self.h, self.d_r), dt[self.dtype]),
+                  ("w_uk", w_uk, (self.h, self.d_h, self.d_c), dt[self.dtype]),
+                  ("w_uv", w_uv, (self.h, self.d_h, self.d_c), dt[self.dtype]),
+                  ("out", out, (T, self.h, self.d_h), dt[self.out_dtype]))
+        for name, t, shape, want in checks:
+            if t.dtype != want or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+                raise ValueError("%s must be a contiguous CUDA tensor of %s with shape %s" % (name, want, shape))
+        need = mla_prefill_workspace_size(T, self.h, self.d_h, self.dtype)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 256), dtype=torch.uint8, device=latent.device)
+        return mla_prefill_run(T, self.h, self.d_c, self.d_r, self.d_h, latent, rope, q, q_r, w_uk, w_uv, out,
+                               self._ws, dtype=self.dtype, out_dtype=self.out_dtype, scale=self.scale, stream=stream)
 
 
 def mla_decode_destroy(plan) -> None:

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"
 
 SOURCES = ["decode.cpp", "q_absorb.hip", "split_attn.hip", "finish.hip", "combine.hip",
-           "general.hip", "oproj.hip", "rope_proj.hip"]
+           "general.hip", "oproj.hip", "rope_proj.hip", "prefill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -592,6 +592,64 @@ mla_status_t mla_query_project_run(int32_t rows, int32_t d_model, int32_t d_qc, 
   return MLA_OK;
 }
 
+size_t mla_prefill_workspace_size(int32_t T, int32_t h, int32_t d_h, int32_t dtype) {
+  g_last_error.clear();
+  if (T < 0 || h < 1 || d_h < 1 || (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32)) {
+    fail(MLA_ERR_INVALID_ARG, "bad prefill shape or dtype");
+    return 0;
+  }
+  return mla::prefill_workspace_bytes(T, h, d_h, dtype == MLA_DTYPE_BF16);
+}
+
+mla_status_t mla_prefill_run(int32_t T, int32_t h, int32_t d_c, int32_t d_r, int32_t d_h, int32_t dtype,
+                             int32_t out_dtype, float scale, const void* latent, const void* rope, const void* q,
+                             const void* q_r, const void* w_uk, const void* w_uv, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (T < 0 || h < 1 || d_c < 1 || d_r < 0 || d_h < 1)
+    return fail(MLA_ERR_INVALID_ARG, "T >= 0, h, d_c, d_h >= 1 and d_r >= 0 are required");
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (out_dtype != -1 && out_dtype != MLA_DTYPE_BF16 && out_dtype != MLA_DTYPE_F32)
+    return fail(MLA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  if (!(scale >= 0.f) || std::isinf(scale)) return fail(MLA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  if ((long long)T * h * d_h > (1LL << 31)) return fail(MLA_ERR_UNSUPPORTED, "prefill larger than this build indexes");
+  if (T == 0) return MLA_OK;
+  if (!latent || !q || !w_uk || !w_uv || !out || !workspace || (d_r > 0 && (!rope || !q_r)))
+    return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const size_t need = mla::prefill_workspace_bytes(T, h, d_h, bf16);
+  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const bool fast = mla::prefill_fast(d_c, d_r, d_h, bf16);
+  const size_t al = fast ? 16 : (bf16 ? 2 : 4);
+  const void* vec[] = {latent, q, w_uk, w_uv, out};
+  for (const void* v : vec)
+    if (!aligned(v, al)) return fail(MLA_ERR_INVALID_ARG, "misaligned tensor (%zu-byte alignment needed)", al);
+  if (d_r > 0 && (!aligned(rope, al) || !aligned(q_r, al))) return fail(MLA_ERR_INVALID_ARG, "misaligned RoPE tensor");
+  mla::PrefillLaunch p;
+  p.latent = latent;
+  p.rope = rope;
+  p.q = q;
+  p.q_r = q_r;
+  p.w_uk = w_uk;
+  p.w_uv = w_uv;
+  p.out = out;
+  p.T = T;
+  p.h = h;
+  p.d_c = d_c;
+  p.d_r = d_r;
+  p.d_h = d_h;
+  p.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)(d_h + d_r));
+  p.bf16 = bf16;
+  p.out_bf16 = (out_dtype == -1 ? dtype : out_dtype) == MLA_DTYPE_BF16;
+  p.work = workspace;
+  mla::LaunchCtx lc;
+  lc.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = mla::launch_prefill(p, lc);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
 mla_status_t mla_decode_enable_timing(mla_decode_t plan, int32_t max_runs) {
   g_last_error.clear();
   if (!plan) return fail(MLA_ERR_INVALID_ARG, "plan is NULL");

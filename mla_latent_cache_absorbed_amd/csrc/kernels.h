@@ -150,4 +150,23 @@ struct QueryLaunch {
 size_t query_project_workspace_bytes(int rows, int d_model, int d_qc, int h, int d_h, int d_r, bool bf16);
 hipError_t launch_query_project(const QueryLaunch& p, const LaunchCtx& s);
 
+// Prefill attention over a prompt of T tokens (prefill.hip): K and V rebuilt
+// from the latents, then causal attention over d_h + d_r dims.
+struct PrefillLaunch {
+  const void* latent;  // [T][d_c]
+  const void* rope;    // [T][d_r] (rotated)
+  const void* q;       // [T][h][d_h]
+  const void* q_r;     // [T][h][d_r]
+  const void* w_uk;    // [h][d_h][d_c]
+  const void* w_uv;    // [h][d_h][d_c]
+  void* out;           // [T][h][d_h]
+  int T = 0, h = 0, d_c = 0, d_r = 0, d_h = 0;
+  float scale = 0.f;
+  bool bf16 = true, out_bf16 = true;
+  void* work;  // prefill_workspace_bytes: K then V, [T][h][d_h] each
+};
+bool prefill_fast(int d_c, int d_r, int d_h, bool bf16);
+size_t prefill_workspace_bytes(int T, int h, int d_h, bool bf16);
+hipError_t launch_prefill(const PrefillLaunch& p, const LaunchCtx& s);
+
 }  // namespace mla

@@ -267,3 +267,25 @@ def make_projections(rows: int, d_model: int = D_MODEL, d_c: int = 512, d_r: int
         out = {k: bf16_bits(v) for k, v in out.items()}
     out.update(dtype=dtype, rows=rows, d_model=d_model, d_c=d_c, d_r=d_r, d_qc=d_qc, h=h, d_h=d_h)
     return out
+
+
+# --------------------------------------------------------------------------
+# Prefill (attention over a whole prompt)
+# --------------------------------------------------------------------------
+def make_prefill(T: int, h: int = 128, d_c: int = 512, d_r: int = 64, d_h: int = 128, dtype: str = "bf16",
+                 seed: int = 500) -> dict:
+    """A prompt of T tokens: latents [T][d_c] and rotated RoPE keys [T][d_r]
+    ~ N(0, 1), queries [T][h][d_h] and RoPE queries [T][h][d_r] ~ N(0, 1),
+    then W_UK, W_UV [h][d_h][d_c] ~ N(0, 1/d_c), drawn in that order (the
+    decode workloads' distributions), bf16 patterns or float32."""
+    rng = np.random.default_rng(seed)
+    out = dict(latent=rng.standard_normal((T, d_c), dtype=np.float32),
+               rope=rng.standard_normal((T, d_r), dtype=np.float32),
+               q=rng.standard_normal((T, h, d_h), dtype=np.float32),
+               q_r=rng.standard_normal((T, h, d_r), dtype=np.float32))
+    for k in ("w_uk", "w_uv"):
+        out[k] = (rng.standard_normal((h, d_h, d_c), dtype=np.float32) / np.float32(np.sqrt(d_c))).astype(np.float32)
+    if dtype == "bf16":
+        out = {k: bf16_bits(v) for k, v in out.items()}
+    out.update(dtype=dtype, T=T, h=h, d_c=d_c, d_r=d_r, d_h=d_h)
+    return out

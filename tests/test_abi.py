@@ -23,7 +23,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj|cache_append|query_project)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj|cache_append|query_project|prefill)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -229,3 +229,14 @@ def test_projections_refuse_bad_calls_on_the_host(L):
                                       workspace_bytes=need - 1, stream=0)
     assert e.value.status == binding.MLA_ERR_WORKSPACE
     assert binding.mla_query_project_run(0, 5120, 1536, 128, 128, 64, *([None] * 7), stream=0) == binding.MLA_OK
+
+
+def test_prefill_refuses_bad_calls_on_the_host(L):
+    assert binding.mla_prefill_workspace_size(4096, 128, 128) == 2 * 4096 * 128 * 128 * 2
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_prefill_run(16, 0, 512, 64, 128, *([None] * 8), stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    with pytest.raises(binding.MLAError) as e:
+        binding.mla_prefill_run(16, 2, 512, 64, 128, *([4096] * 7), 4096, workspace_bytes=16, stream=0)
+    assert e.value.status == binding.MLA_ERR_WORKSPACE
+    assert binding.mla_prefill_run(0, 2, 512, 64, 128, *([None] * 8), stream=0) == binding.MLA_OK

@@ -401,6 +401,49 @@ def measure_projections(rows, runs, warmup):
     return out
 
 
+def measure_prefill(T, runs, warmup, h=128):
+    """Prefill (keys and values rebuilt, causal attention) of a T-token
+    prompt at DeepSeek-V2 head shapes: per-call events on the launch stream
+    over `runs` calls."""
+    import torch
+    from mla_latent_cache_absorbed_amd import binding, inputs
+    case = inputs.make_prefill(T, h=h, seed=560)
+    d_c, d_r, d_h = case["d_c"], case["d_r"], case["d_h"]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    t = {k: dev(case[k]) for k in ("latent", "rope", "q", "q_r", "w_uk", "w_uv")}
+    out = torch.empty((T, h, d_h), dtype=torch.bfloat16, device="cuda")
+    need = binding.mla_prefill_workspace_size(T, h, d_h)
+    work = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    L = binding.lib()
+    args = (T, h, d_c, d_r, d_h, binding.MLA_DTYPE_BF16, binding.MLA_DTYPE_BF16, 0.0, t["latent"].data_ptr(),
+            t["rope"].data_ptr(), t["q"].data_ptr(), t["q_r"].data_ptr(), t["w_uk"].data_ptr(), t["w_uv"].data_ptr(),
+            out.data_ptr(), work.data_ptr(), need, stream)
+    for _ in range(warmup):
+        binding.raise_for_status(L.mla_prefill_run(*args))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * runs)]
+    torch.cuda.synchronize()
+    status = 0
+    for i in range(runs):
+        ev[2 * i].record()
+        status = min(status, L.mla_prefill_run(*args))
+        ev[2 * i + 1].record()
+    binding.raise_for_status(status)
+    torch.cuda.synchronize()
+    st = stats([ev[2 * i].elapsed_time(ev[2 * i + 1]) / 1e3 for i in range(runs)])
+    rebuild = 2 * 2 * T * d_c * h * d_h                   # K and V from the latents
+    attn = h * (T * (T + 1) // 2) * 2 * (d_h + d_r + d_h)  # causal scores over d_h + d_r, weighted values
+    flops = rebuild + attn
+    return dict(T=T, h=h, us={k: st[k] * 1e6 for k in ("mean", "median", "p10", "p90")}, runs=st["n"],
+                algorithmic_flops=flops, rebuild_flops=rebuild, attention_flops=attn,
+                roofline=dict(bound="mfma", achieved=flops / st["median"] / 1e12, peak=MFMA_BF16_TFLOPS,
+                              unit="TFLOP/s", frac=flops / st["median"] / 1e12 / MFMA_BF16_TFLOPS,
+                              what="median over the runs of one call (rebuild GEMM + attention)"))
+
+
 def achievable_peaks():
     """What plain library work reaches on this GPU, for context beside the
     vendor peaks: a 1 GiB device-to-device copy (read + write bytes) and a
@@ -583,6 +626,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-oproj", action="store_true", help="skip the output-projection measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--prefill-only", type=int, default=0, metavar="T",
+                    help="only time prefill of a T-token prompt (for profiling) and print its record")
     ap.add_argument("--no-projections", action="store_true",
                     help="skip the cache-append and query-side measurements")
     ap.add_argument("--projections-only", type=int, default=0, metavar="ROWS",
@@ -625,6 +671,9 @@ def main():
 
     if args.oproj_only:
         print(json.dumps(measure_oproj(args.oproj_only, dist_runs, args.warmup)))
+        return
+    if args.prefill_only:
+        print(json.dumps(measure_prefill(args.prefill_only, max(5, args.steps), args.warmup)))
         return
     if args.projections_only:
         print(json.dumps(measure_projections(args.projections_only, dist_runs, args.warmup)))
@@ -736,6 +785,10 @@ def main():
         # projection of the headline's rows and of the batched configurations'
         out["oproj"] = {"r%d" % r: measure_oproj(r, dist_runs, 10) for r in (1, 32, 64)}
         log("oproj (median us): %s" % {k: round(v["us"]["median"], 2) for k, v in out["oproj"].items()})
+    if not args.no_prefill:
+        # prefill of a 4K-token prompt (the T=4K decode configuration's context)
+        out["prefill"] = {"t4k": measure_prefill(4096, 20, 3)}
+        log("prefill T=4096 (median us): %.1f" % out["prefill"]["t4k"]["us"]["median"])
     if not args.no_projections:
         # the steps before the decode path, measured on their own: the cache
         # append and the query side of one and of 64 new tokens

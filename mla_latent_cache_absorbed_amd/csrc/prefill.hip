@@ -64,8 +64,11 @@ struct GemmArgs {
   int rows, k, n;
 };
 
-// 16-byte chunk c of staged row r is stored at chunk c ^ (r & 7).
-__device__ __forceinline__ uint32_t gemm_off(int r, int c) { return (uint32_t)r * kGemmRowBytes + 16u * (uint32_t)(c ^ (r & 7)); }
+// 16-byte chunk c of staged row r (128 bytes) is stored at chunk
+// c ^ ((r >> 1) & 7): two rows share each 256-byte bank period, so the 16
+// rows one operand read serves at a time land in 16 different slots.
+__device__ __forceinline__ int gemm_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ uint32_t gemm_off(int r, int c) { return (uint32_t)r * kGemmRowBytes + 16u * (uint32_t)(c ^ gemm_swz(r)); }
 
 __global__ __launch_bounds__(kThreads) void kv_rebuild_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kGemmTileBytes];  // [stage][x | w]
@@ -79,8 +82,8 @@ __global__ __launch_bounds__(kThreads) void kv_rebuild_kernel(GemmArgs a) {
   uint16_t* dst = a.out[blockIdx.z];
 
   // DMA: one instruction fills 8 staged rows of 128 bytes (lane l writes
-  // slot l % 8 of row l / 8, which holds chunk (l % 8) ^ (row & 7): the lane
-  // reads that chunk); a stage is 16 instructions per operand, 8 per wave
+  // slot l % 8 of row l / 8, which holds chunk (l % 8) ^ gemm_swz(row): the
+  // lane reads that chunk); a stage is 16 instructions per operand, 8 per wave
   const uint32_t lds_base = (uint32_t)(uintptr_t)((AS3 uint8_t*)lds);
   auto issue = [&](int stage, int kk) {
 #pragma unroll
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void kv_rebuild_kernel(GemmArgs a) {
       const int base = op == 0 ? t0 : n0;
       const int lim = op == 0 ? a.rows : a.n;
       const int rr = base + r < lim ? r : lim - 1 - base;  // rows past the end repeat the last (never stored)
-      const uint32_t voff = ((uint32_t)rr * (uint32_t)a.k + 8u * (uint32_t)((lane & 7) ^ (r & 7))) * 2u;
+      const uint32_t voff = ((uint32_t)rr * (uint32_t)a.k + 8u * (uint32_t)((lane & 7) ^ gemm_swz(r))) * 2u;
       const uint16_t* sbase = (op == 0 ? a.x + (size_t)t0 * a.k : wsrc + (size_t)n0 * a.k) + kk;
       lds_dma16(sbase, voff, lds_base + (uint32_t)((stage * 2 + op) * kGemmTileBytes + grp * 8 * kGemmRowBytes));
     }
@@ -191,10 +194,10 @@ struct AttnArgs {
 
 // LDS layouts of a stage (16-byte chunks XOR-swizzled by row):
 // K rows (256 B): chunk c of row r at c ^ (r & 15)      (score operand reads)
-// K_R rows (128 B): chunk c at c ^ (r & 7)
+// K_R rows (128 B): chunk c at c ^ ((r >> 1) & 7) (two rows per bank period)
 // V rows (256 B): chunk c at c ^ (4 (r & 3))             (transposing reads)
 __device__ __forceinline__ uint32_t k_off(int r, int c) { return (uint32_t)r * 256u + 16u * (uint32_t)(c ^ (r & 15)); }
-__device__ __forceinline__ uint32_t r_off(int r, int c) { return (uint32_t)r * 128u + 16u * (uint32_t)(c ^ (r & 7)); }
+__device__ __forceinline__ uint32_t r_off(int r, int c) { return (uint32_t)r * 128u + 16u * (uint32_t)(c ^ ((r >> 1) & 7)); }
 __device__ __forceinline__ uint32_t v_off(int r, int col) {
   return (uint32_t)r * 256u + 16u * (uint32_t)((col >> 3) ^ (4 * (r & 3))) + 8u * (uint32_t)((col >> 2) & 1);
 }
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_attn_kernel(AttnArgs a) {
         const int grp = d - 8;                   // 8-row group
         const int r = 8 * grp + (lane >> 3);
         const int key = min(k0 + r, a.T - 1);
-        const int c = (lane & 7) ^ (r & 7);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         const uint32_t voff = (uint32_t)(key - k0) * (kDr * 2) + 16u * (uint32_t)c;
         lds_dma16(a.kr + (size_t)k0 * kDr, voff, ring_base + (uint32_t)(stage * kStageBytes + kKBytes + grp * 1024));
       }
@@ -291,14 +294,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_attn_kernel(AttnArgs a) {
     }
     // ---- online softmax of the lane's query (base 2) ----
     const int k0 = it * kKeyTile;
-    const int query = qw + l32;
     float tmax = -INFINITY;
+    if (k0 + kKeyTile > qw || k0 + kKeyTile > a.T) {  // the wave's diagonal tile, or the prompt's last
+      const int query = qw + l32;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int key = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
-      const float v = (key <= query && key < a.T) ? sc[j] * a.scale_log2 : -INFINITY;
-      sc[j] = v;
-      tmax = fmaxf(tmax, v);
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + 8 * (j >> 2) + 4 * hi + (j & 3);
+        const float v = (key <= query && key < a.T) ? sc[j] * a.scale_log2 : -INFINITY;
+        sc[j] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        sc[j] *= a.scale_log2;
+        tmax = fmaxf(tmax, sc[j]);
+      }
     }
     {
       auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);

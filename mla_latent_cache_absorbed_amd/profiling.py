@@ -45,6 +45,8 @@ KERNELS = {
     "combine": ("combine_general", ("combine.hip",)),
     "up_project": ("up_general", ("general.hip",)),
     "oproj": ("oproj_", ("oproj.hip",)),
+    "prefill_attn": ("prefill_attn", ("prefill.hip",)),
+    "kv_rebuild": ("kv_rebuild", ("prefill.hip",)),
 }
 
 

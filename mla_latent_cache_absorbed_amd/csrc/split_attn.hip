@@ -35,8 +35,8 @@
 //   registers; tiles k+1 and k+2 are in flight while the score waves read
 //   tile k and the accumulate waves tile k-1.  A DMA instruction holds its
 //   wave at issue while the CU's fetch path is busy, so the accumulate
-//   waves issue a tile's DMAs after their MFMAs, while the score waves do
-//   the softmax arithmetic.  A tile never straddles a cache page (pages are
+//   waves issue a tile's DMAs first in each iteration, while the score
+//   waves' MFMAs run.  A tile never straddles a cache page (pages are
 //   multiples of 32 tokens), so each tile is one contiguous run of 32
 //   latent rows and 32 RoPE rows in the pool; every tile's pool row is
 //   looked up once at the start.
@@ -96,11 +96,13 @@ constexpr int kStageBytes = kLatBytes + kRopeBytes;
 constexpr int kLatRowsPerWave = kTile / kAccWaves;   // 4
 constexpr int kRopeRowsPerWave = kTile / kAccWaves;  // 4
 constexpr int kAccDmas = kLatRowsPerWave + 1;        // 5
+
 // LDS operand reads kept in flight, in pairs (lgkmcnt counts at most 15)
 constexpr int kScoreReadsAhead = 6;
 constexpr int kAccReadsAhead = 6;
 
 static_assert(kBlocks == 4 && kTile == 32, "load mapping assumes 4 head blocks and 32-token tiles");
+
 // The absorbed query of the group (64 rows of 1 KB, then 64 RoPE rows of
 // 128 B) passes through ring stages kQStage.. during the prologue.
 constexpr int kQStage = 2;
@@ -309,10 +311,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
   // written by the score waves between barriers k and k + 1, read by the
   // accumulate waves between barriers k + 1 and k + 2, and overwritten
   // (tile k + 2) only after that.  The accumulate waves issue tile it + 2
-  // between barriers it and it + 1 (after folding tile it - 1), into the
+  // between barriers it and it + 1 (before folding tile it - 1), into the
   // stage that tile it - 2 (finished before barrier it) occupied, and wait
-  // for their share of tile it + 1 before barrier it + 1.  Each role keeps all of its state inside its own branch,
-  // so that nothing of one role is live across the other's loop.
+  // for their share of tile it + 1 before barrier it + 1.  Each role keeps
+  // all of its state inside its own branch, so that nothing of one role is
+  // live across the other's loop.
   if (scorer) {
     // ---- prologue: this wave's 16 absorbed-query rows (and their RoPE
     //      parts) come into ring stages 2-3 by DMA, whole 1 KB rows per
@@ -421,8 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       // max: it moves only when a score exceeds it by more than
       // kRescaleSlack, so weights stay below 2^kRescaleSlack and most tiles
       // need no rescale.  The final division by l makes the result
-      // independent of the reference.  Scores stay unscaled until the
-      // exponent (scale > 0, so maxima commute with it).
+      // independent of the reference.
       const int slot = it & 1;
       if (ts + kTile > t1) {  // the chunk's last tile: tokens past t1 weigh 0
 #pragma unroll
@@ -431,10 +433,19 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
           for (int j = 0; j < 4; ++j)
             if (ts + tb * 16 + 4 * g + j >= t1) sacc[tb][j] = -INFINITY;
       }
-      float tmax = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                         fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
-      tmax = max_over_token_lanes(tmax) * p.scale_log2;
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
+      // Scaled scores (base 2); the product is a canonical float, so the
+      // maxima below need no NaN quieting.
+      f32x4 ss[2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) ss[tb] = sacc[tb] * p.scale_log2;
+      // This lane's maximum over its 8 tokens.  Some head's tile maximum
+      // exceeds its reference by more than the slack exactly when some
+      // lane's does, so the cross-lane reduction runs only on the tiles
+      // where a reference moves (the first, and rarely after it).
+      const float lmax = fmaxf(fmaxf(fmaxf(ss[0][0], ss[0][1]), fmaxf(ss[0][2], ss[0][3])),
+                               fmaxf(fmaxf(ss[1][0], ss[1][1]), fmaxf(ss[1][2], ss[1][3])));
+      if (__builtin_amdgcn_ballot_w64(lmax > m_run + kRescaleSlack) != 0) {  // wave-uniform
+        const float tmax = max_over_token_lanes(lmax);  // the head's tile maximum
         const float m_new = fmaxf(m_run, tmax);
         // nothing has been accumulated before the first tile: no rescale
         const int flag = m_run != -INFINITY;
@@ -453,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          pf[tb * 4 + j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[tb][j], p.scale_log2, -m_run));
+          pf[tb * 4 + j] = __builtin_amdgcn_exp2f(ss[tb][j] - m_run);
       const bf16x8 pb = __builtin_convertvector(pf, bf16x8);  // round to nearest even
       sh.prob[slot][blk][lane] = __builtin_bit_cast(u32x4, pb);
       // sum of the weights the MFMA sees (bf16), two per dot2
@@ -537,6 +548,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       }
       continue;
     }
+    // Tile it + 2 goes out before the fold: a DMA holds its wave at issue
+    // while the CU's fetch path is busy, and here that time overlaps the
+    // score waves' MFMAs (issued after the fold, it delayed the barrier by
+    // the whole hold: 4-9 % longer loop at T = 32K..128K and in MTP).
+    if (more) {
+#pragma unroll
+      for (int part = 0; part < kAccDmas; ++part) dma(it + 2, row_next, t1, part, lat_voff);
+    }
     const int j = it - 1;  // tile folded in this iteration
     const int slot = j & 1;
     const AS3 uint8_t* stage = (const AS3 uint8_t*)sh.ring + (j % kStages) * kStageBytes;
@@ -550,10 +569,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       return as_bf16x8(v);
     };
     // The four rescale flags, P(j) and the first latent operands go out
-    // together and the MFMAs follow; the tile DMAs come last (a DMA holds
-    // the wave at issue while the CU's fetch path is busy, which at the
-    // start of the iteration delayed the MFMAs; at the end it overlaps the
-    // score waves' softmax).
+    // together and the MFMAs follow.
     const u32x4 flags = sh.rescale[slot];
     bf16x8 pb[kBlocks];
 #pragma unroll
@@ -582,10 +598,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_attn_bf16_kernel(SplitArgs 
       for (int hb = 0; hb < kBlocks; ++hb)
         acc[fb][hb] = mfma16x16x32(opq[fb % (kAhead + 1)], pb[hb], acc[fb][hb]);
       __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) {
-#pragma unroll
-      for (int part = 0; part < kAccDmas; ++part) dma(it + 2, row_next, t1, part, lat_voff);
     }
   }
   block_barrier();  // pairs with the score waves' barrier after their lse

@@ -78,23 +78,6 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
       : "memory");
 }
 
-// The same DMA with 4 bytes per lane (global_load_lds_dword): lane l
-// reads sbase + voff[l] and writes lds_base + 4 l.  With the lanes 128
-// bytes apart, one instruction brings 64 cache lines towards the CU (a
-// prefetch into L2 when the LDS copy is a throw-away).
-__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "v"(voff), "s"(sbase)
-      : "memory");
-}
-
 // Wave-wide reductions over lanes that differ in the given xor bit(s).
 __device__ __forceinline__ float xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);

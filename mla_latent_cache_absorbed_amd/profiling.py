@@ -41,12 +41,13 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 KERNELS = {
     "q_absorb": ("q_absorb", ("q_absorb.hip",)),
     "split_attn": ("split_attn", ("split_attn.hip",)),
-    "finish": ("finish", ("finish.hip",)),
+    "finish": ("finish_bf16", ("finish.hip",)),
     "combine": ("combine_general", ("combine.hip",)),
     "up_project": ("up_general", ("general.hip",)),
     "oproj": ("oproj_", ("oproj.hip",)),
     "prefill_attn": ("prefill_attn", ("prefill.hip",)),
     "kv_rebuild": ("kv_rebuild", ("prefill.hip",)),
+    "rope_finish": ("rope_finish", ("rope_proj.hip",)),
 }
 
 

@@ -233,6 +233,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_attn_kernel(AttnArgs a) {
     const uint16_t* qrp = a.qr + ((size_t)qq * a.h + head) * kDr + 8 * hi;
 #pragma unroll
     for (int s = 0; s < 4; ++s) qv[8 + s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrp + 16 * s));
+    // Consume the query registers here: the compiler then waits for these
+    // loads once, before the loop.  (Its waits for them inside the loop
+    // count the tile DMAs too, which it cannot see, and so made every tile
+    // wait for the DMAs just issued for tile it + 2.)
+#pragma unroll
+    for (int s = 0; s < 12; ++s) asm volatile("" ::"v"(qv[s]));
   }
 
   // tile DMAs: per tile 8 KB of K (8 instructions of 4 rows), 4 KB of K_R (4

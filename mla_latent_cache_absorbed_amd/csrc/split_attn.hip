@@ -98,7 +98,7 @@ constexpr int kRopeRowsPerWave = kTile / kAccWaves;  // 4
 constexpr int kAccDmas = kLatRowsPerWave + 1;        // 5
 
 // LDS operand reads kept in flight, in pairs (lgkmcnt counts at most 15)
-constexpr int kScoreReadsAhead = 6;
+constexpr int kScoreReadsAhead = 4;
 constexpr int kAccReadsAhead = 6;
 
 static_assert(kBlocks == 4 && kTile == 32, "load mapping assumes 4 head blocks and 32-token tiles");

@@ -44,7 +44,12 @@ constexpr int kWaves = 4;
 constexpr int kFeatures = 64;  // output features per work-group
 constexpr int kNb = kFeatures / 16;
 constexpr int kRowsPerGroup = 64;
-constexpr int kDepth = 4;      // k-steps of loads in flight per wave
+// k-steps of loads in flight per wave: four, or two with four 16-row
+// blocks (so that a wave stays within 256 registers and two work-groups
+// share a CU); either divides a wave's steps, a multiple of four
+constexpr int kMaxDepth = 4;
+template <int kRb>
+constexpr int depth_for() { return kRb >= 4 ? 2 : kMaxDepth; }
 
 struct OprojArgs {
   const uint16_t* o;   // [rows][k]
@@ -57,6 +62,7 @@ struct OprojArgs {
 
 template <int kRb>  // 16-row blocks per work-group (1, 2 or 4)
 __global__ __launch_bounds__(kThreads) void oproj_partial_kernel(OprojArgs a) {
+  constexpr int kDepth = depth_for<kRb>();
   __shared__ __attribute__((aligned(16))) f32x4 red[kWaves][kNb][kRb][64];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -177,7 +183,7 @@ int splits_for(int rows, int k, int d) {
   // at k = 16384, d = 5120: 1, 32 and 64 rows ran 2-8 % faster than with 8
   // slices, and 32 slices slower again), else the most there can be; every
   // wave keeps whole unrolled k-steps, so the count divides k / 512.
-  const int units = k / (kWaves * 32 * kDepth);
+  const int units = k / (kWaves * 32 * kMaxDepth);
   for (int s = 1; s <= units; ++s)
     if (units % s == 0 && groups * s >= 1024) return s;
   return units;
@@ -214,7 +220,7 @@ hipError_t launch_partial(const void* x, const void* w0, const void* w1, int row
 
 }  // namespace
 
-bool oproj_fast_applies(int k, int d, bool bf16) { return bf16 && d % kFeatures == 0 && k % (kWaves * 32 * kDepth) == 0; }
+bool oproj_fast_applies(int k, int d, bool bf16) { return bf16 && d % kFeatures == 0 && k % (kWaves * 32 * kMaxDepth) == 0; }
 
 
 hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s) {

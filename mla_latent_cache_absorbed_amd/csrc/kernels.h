@@ -56,11 +56,17 @@ struct LaunchCtx {
 };
 
 template <typename Kernel, typename... Args>
-inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, const LaunchCtx& c, Args... args) {
+inline void launch_kernel_lds(Kernel kernel, dim3 grid, dim3 block, size_t lds_bytes, const LaunchCtx& c,
+                              Args... args) {
   if (c.start && c.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, c.stream, c.start, c.stop, 0, args...);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, c.stream, c.start, c.stop, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, c.stream, args...);
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, c.stream, args...);
+}
+
+template <typename Kernel, typename... Args>
+inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, const LaunchCtx& c, Args... args) {
+  launch_kernel_lds(kernel, grid, block, 0, c, args...);
 }
 
 // Heads handled by one work-group of the fast split kernel.

@@ -30,10 +30,14 @@
 //   work-group writes an fp32 partial and a second kernel sums the S
 //   partials of each output in slice order, so the result does not depend
 //   on timing.  S is chosen so that the grid has at least 1024 work-groups.
+// - Up to kRowsDotMaxRows rows (with x within 64 KB), one launch without
+//   slices instead: one wave per two output features over the whole of k
+//   (rows_dot.h), no partials.
 // - Shapes outside d % 64 == 0 and k % 512 == 0, and fp32 storage, take a
 //   plain kernel: one thread per output, an fp32 dot product over k.
 #include "common.h"
 #include "kernels.h"
+#include "rows_dot.h"
 
 namespace mla {
 
@@ -146,6 +150,27 @@ __global__ __launch_bounds__(kThreads) void oproj_partial_kernel(OprojArgs a) {
   }
 }
 
+// Up to kR rows (rows_dot_applies): wave = output features n, n + 1 over the
+// whole of k; lane r stores row r.
+template <int kR, bool kLds, int kDepth>
+__global__ __launch_bounds__(kRowsDotWaves * 64) void oproj_rows_kernel(OprojArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t x_lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = kRowsDotFeatures * (blockIdx.x * kRowsDotWaves + wave);  // < d: the grid is d / 8
+  const uint16_t* w = a.w + (size_t)n * a.k;
+  float s[kRowsDotFeatures][kR];
+  rows_dot<kR, kLds, kDepth>(a.o, a.rows, a.k, w, w + a.k, x_lds, s);
+  if (lane >= a.rows) return;
+  float v0, v1;
+  rows_dot_pick<kR>(s, lane, v0, v1);
+  const size_t idx = (size_t)lane * a.d + n;
+  if (a.out_bf16)
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.u) + idx) = pack_bf16x2(v0, v1);
+  else
+    *reinterpret_cast<f32x2*>(static_cast<float*>(a.u) + idx) = f32x2{v0, v1};
+}
+
 // u = sum over the S slices of the partials, in slice order; four
 // consecutive outputs per thread (d % 64 == 0).
 __global__ __launch_bounds__(kThreads) void oproj_reduce_kernel(OprojArgs a) {
@@ -220,6 +245,8 @@ hipError_t launch_partial(const void* x, const void* w0, const void* w1, int row
 
 }  // namespace
 
+static_assert((kWaves * 32 * kMaxDepth) % kRowsDotK == 0, "the few-row kernel steps through k in 512s");
+
 bool oproj_fast_applies(int k, int d, bool bf16) { return bf16 && d % kFeatures == 0 && k % (kWaves * 32 * kMaxDepth) == 0; }
 
 
@@ -245,6 +272,31 @@ hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s) {
     return hipGetLastError();
   }
   OprojArgs a;
+  if (rows_dot_applies(p.rows, p.k, p.d)) {
+    a.o = static_cast<const uint16_t*>(p.o);
+    a.w = static_cast<const uint16_t*>(p.w);
+    a.w1 = nullptr;
+    a.part = nullptr;
+    a.u = p.u;
+    a.rows = p.rows;
+    a.k = p.k;
+    a.d = p.d;
+    a.d0 = p.d;
+    a.splits = 1;
+    a.out_bf16 = p.out_bf16;
+    a.write_part = 0;
+    const dim3 grid(p.d / kRowsDotPerGroup), block(kRowsDotWaves * 64);
+    const size_t lds = rows_dot_lds_bytes(p.rows, p.k);
+    if (lds > 0)  // three or four rows of x, staged in LDS
+      launch_kernel_lds(oproj_rows_kernel<4, true, kRowsDotDepth>, grid, block, lds, s, a);
+    else if (rows_dot_deep(p.rows, p.k))  // one or two rows of x, read from L2
+      launch_kernel(oproj_rows_kernel<1, false, kRowsDotDeepDepth>, grid, block, s, a);
+    else if (p.rows == 1)
+      launch_kernel(oproj_rows_kernel<1, false, kRowsDotDepth>, grid, block, s, a);
+    else
+      launch_kernel(oproj_rows_kernel<2, false, kRowsDotDepth>, grid, block, s, a);
+    return hipGetLastError();
+  }
   const hipError_t e = launch_partial(p.o, p.w, nullptr, p.rows, p.k, p.d, p.d, static_cast<float*>(p.part), false,
                                       p.u, p.out_bf16, s, &a);
   if (e != hipSuccess) return e;
@@ -263,7 +315,7 @@ hipError_t launch_proj_partial(const void* x, const void* w0, const void* w1, in
 }
 
 size_t oproj_workspace_bytes(int rows, int k, int d, bool bf16) {
-  if (!oproj_fast_applies(k, d, bf16)) return 0;
+  if (!oproj_fast_applies(k, d, bf16) || rows_dot_applies(rows, k, d)) return 0;
   const int s = oproj_splits(rows, k, d);
   return s > 1 ? (size_t)s * rows * d * sizeof(float) : 0;
 }

@@ -31,9 +31,13 @@
 // ([W_DKV; W_KR], [W_UQ; W_QR]); a finish kernel here sums its fp32 slice
 // partials in slice order, applies RoPE to the second weight's features
 // and writes bf16 to the pools (cache append) or to q and q_R (query side).
-// Other shapes and fp32 storage run one plain kernel per stage.
+// Up to kRowsDotMaxRows rows (with x within 64 KB) a stage is one launch
+// instead: one wave per two adjacent output features over the whole of k
+// (rows_dot.h), with the RoPE pair and the store in the same kernel.  Other shapes and fp32
+// storage run one plain kernel per stage.
 #include "common.h"
 #include "kernels.h"
+#include "rows_dot.h"
 
 namespace mla {
 
@@ -115,6 +119,51 @@ __global__ __launch_bounds__(kThreads) void rope_finish_kernel(FinishArgs a) {
   *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
+// Up to kR rows: wave = output features n, n + 1 of the stacked weights
+// [w0; w1] over the whole of k (n even, so a RoPE pair stays in one wave);
+// lane r finishes row r.
+struct RowsArgs {
+  const uint16_t* x;   // [rows][k]
+  const uint16_t* w0;  // [n0][k]
+  const uint16_t* w1;  // [n1][k]
+  int rows, k, n0, n1, d_r;
+  const int32_t* pos;
+  const double* theta;
+  double base;
+  Dest dst;
+};
+
+template <int kR, bool kLds, int kDepth>
+__global__ __launch_bounds__(kRowsDotWaves * 64) void rope_rows_kernel(RowsArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t x_lds[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = kRowsDotFeatures * (blockIdx.x * kRowsDotWaves + wave);  // < n0 + n1: the grid is (n0 + n1) / 8
+  const uint16_t* w = n < a.n0 ? a.w0 + (size_t)n * a.k : a.w1 + (size_t)(n - a.n0) * a.k;
+  float sums[kRowsDotFeatures][kR];
+  rows_dot<kR, kLds, kDepth>(a.x, a.rows, a.k, w, w + a.k, x_lds, sums);
+  if (lane >= a.rows) return;
+  float v0, v1;
+  rows_dot_pick<kR>(sums, lane, v0, v1);
+  const int t = a.pos[lane];
+  size_t row;
+  if (!dest_row(a.dst, lane, t, row)) return;
+  uint16_t* out;
+  if (n < a.n0) {
+    out = static_cast<uint16_t*>(a.dst.out0) + row * a.n0 + n;
+  } else {
+    const int g = n - a.n0;
+    double sn, cs;
+    sincos((double)t * rope_theta(a.theta, a.base, (g % a.d_r) / 2, a.d_r), &sn, &cs);
+    const float c = (float)cs, si = (float)sn;
+    const float x0 = v0, x1 = v1;
+    v0 = x0 * c - x1 * si;
+    v1 = x1 * c + x0 * si;
+    out = static_cast<uint16_t*>(a.dst.out1) + row * a.n1 + g;
+  }
+  *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(v0, v1);
+}
+
 // Any shape and either storage type: one thread per output feature of the
 // first weight, or per RoPE pair of the second, fp32 dot products over k.
 template <typename T>
@@ -155,6 +204,32 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 hipError_t run_stage(const void* x, const void* w0, const void* w1, int rows, int k, int n0, int n1, int d_r,
                      const int32_t* pos, const double* theta, double base, const Dest& dst, bool bf16, bool fast,
                      float* part, const LaunchCtx& s) {
+  if (fast && rows_dot_applies(rows, k, n0 + n1)) {
+    RowsArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.w0 = static_cast<const uint16_t*>(w0);
+    a.w1 = static_cast<const uint16_t*>(w1);
+    a.rows = rows;
+    a.k = k;
+    a.n0 = n0;
+    a.n1 = n1;
+    a.d_r = d_r;
+    a.pos = pos;
+    a.theta = theta;
+    a.base = base;
+    a.dst = dst;
+    const dim3 grid((n0 + n1) / kRowsDotPerGroup), block(kRowsDotWaves * 64);
+    const size_t lds = rows_dot_lds_bytes(rows, k);
+    if (lds > 0)  // three or four rows of x, staged in LDS
+      launch_kernel_lds(rope_rows_kernel<4, true, kRowsDotDepth>, grid, block, lds, s, a);
+    else if (rows_dot_deep(rows, k))  // one or two rows of x, read from L2
+      launch_kernel(rope_rows_kernel<1, false, kRowsDotDeepDepth>, grid, block, s, a);
+    else if (rows == 1)
+      launch_kernel(rope_rows_kernel<1, false, kRowsDotDepth>, grid, block, s, a);
+    else
+      launch_kernel(rope_rows_kernel<2, false, kRowsDotDepth>, grid, block, s, a);
+    return hipGetLastError();
+  }
   if (fast) {
     hipError_t e = launch_proj_partial(x, w0, w1, rows, k, n0 + n1, n0, part, s);
     if (e != hipSuccess) return e;
@@ -191,7 +266,7 @@ bool stage_fast(int k, int n0, int n1, int d_r, bool bf16) {
 }
 
 size_t stage_part_bytes(int rows, int k, int n, bool fast) {
-  return fast ? (size_t)oproj_splits(rows, k, n) * rows * n * sizeof(float) : 0;
+  return fast && !rows_dot_applies(rows, k, n) ? (size_t)oproj_splits(rows, k, n) * rows * n * sizeof(float) : 0;
 }
 
 }  // namespace

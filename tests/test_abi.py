@@ -188,7 +188,12 @@ def test_last_error_cleared_by_success(L):
 
 def test_output_projection_refuses_bad_calls_on_the_host(L):
     # before any launch: bad sizes, unknown dtype, NULL tensors, missing workspace
-    assert binding.mla_oproj_workspace_size(1, 16384, 5120) == 16 * 5120 * 4  # 16 slices of k
+    assert binding.mla_oproj_workspace_size(8, 16384, 5120) == 16 * 8 * 5120 * 4  # 16 slices of k
+    # one launch, no partials: up to 4 rows whose x fits 40 KB of LDS, or up
+    # to 2 rows of any length (x from L2)
+    assert binding.mla_oproj_workspace_size(2, 16384, 5120) == 0
+    assert binding.mla_oproj_workspace_size(4, 4096, 5120) == 0
+    assert binding.mla_oproj_workspace_size(3, 16384, 5120) == 16 * 3 * 5120 * 4  # 96 KB of x: slices
     assert binding.mla_oproj_workspace_size(1, 64, 40, "f32") == 0           # plain kernel, no partials
     with pytest.raises(binding.MLAError) as e:
         binding.mla_oproj_run(1, 0, 5, None, None, None, stream=0)
@@ -197,15 +202,17 @@ def test_output_projection_refuses_bad_calls_on_the_host(L):
         binding.mla_oproj_run(1, 16384, 5120, None, None, None, stream=0)
     assert e.value.status == binding.MLA_ERR_INVALID_ARG
     with pytest.raises(binding.MLAError) as e:
-        binding.mla_oproj_run(1, 16384, 5120, 4096, 4096, 4096, stream=0)
+        binding.mla_oproj_run(8, 16384, 5120, 4096, 4096, 4096, stream=0)
     assert e.value.status == binding.MLA_ERR_WORKSPACE
-    assert "327680 needed" in binding.mla_decode_last_error()
+    assert "2621440 needed" in binding.mla_decode_last_error()
     assert binding.mla_oproj_run(0, 16384, 5120, None, None, None, stream=0) == binding.MLA_OK  # nothing to do
 
 
 def test_projections_refuse_bad_calls_on_the_host(L):
-    # cache append: 9 MFMA blocks of 64 features, k = 5120 in 10 slices
-    assert binding.mla_cache_append_workspace_size(1, 5120, 512, 64) == 10 * 576 * 4
+    # cache append: 9 MFMA blocks of 64 features, k = 5120 in 10 slices;
+    # up to 4 rows one launch without partials
+    assert binding.mla_cache_append_workspace_size(8, 5120, 512, 64) == 10 * 8 * 576 * 4
+    assert binding.mla_cache_append_workspace_size(1, 5120, 512, 64) == 0
     assert binding.mla_cache_append_workspace_size(4, 5, 2, 2, "f32") == 0
     assert binding.mla_cache_append_workspace_size(1, 5120, 512, 63) == 0  # odd d_r
     with pytest.raises(binding.MLAError) as e:
@@ -215,17 +222,18 @@ def test_projections_refuse_bad_calls_on_the_host(L):
         binding.mla_cache_append_run(1, 5120, 512, 64, *([None] * 6), 4, 64, 8, None, None, stream=0)
     assert e.value.status == binding.MLA_ERR_INVALID_ARG
     with pytest.raises(binding.MLAError) as e:  # no workspace
-        binding.mla_cache_append_run(1, 5120, 512, 64, *([4096] * 6), 4, 64, 8, 4096, 4096, stream=0)
+        binding.mla_cache_append_run(8, 5120, 512, 64, *([4096] * 6), 4, 64, 8, 4096, 4096, stream=0)
     assert e.value.status == binding.MLA_ERR_WORKSPACE
     with pytest.raises(binding.MLAError) as e:  # no frequencies and a base <= 1
         binding.mla_cache_append_run(1, 5120, 512, 64, *([4096] * 6), 4, 64, 8, 4096, 4096, rope_base=1.0,
                                      stream=0)
     assert e.value.status == binding.MLA_ERR_INVALID_ARG
     # query side: c_Q (256-aligned) plus the larger of the two stages' partials
-    need = binding.mla_query_project_workspace_size(1, 5120, 1536, 128, 128, 64)
-    assert need == 3072 + max(10 * 1536 * 4, 3 * 128 * 192 * 4)
+    need = binding.mla_query_project_workspace_size(8, 5120, 1536, 128, 128, 64)
+    assert need == 8 * 3072 + max(10 * 8 * 1536 * 4, 3 * 8 * 128 * 192 * 4)
+    assert binding.mla_query_project_workspace_size(1, 5120, 1536, 128, 128, 64) == 3072  # c_Q only
     with pytest.raises(binding.MLAError) as e:
-        binding.mla_query_project_run(1, 5120, 1536, 128, 128, 64, *([4096] * 7), workspace=4096,
+        binding.mla_query_project_run(8, 5120, 1536, 128, 128, 64, *([4096] * 7), workspace=4096,
                                       workspace_bytes=need - 1, stream=0)
     assert e.value.status == binding.MLA_ERR_WORKSPACE
     assert binding.mla_query_project_run(0, 5120, 1536, 128, 128, 64, *([None] * 7), stream=0) == binding.MLA_OK

@@ -1,8 +1,8 @@
 """GPU parity of the output projection u = [o_1; ...; o_h] W^O (the step
 after the decode path) through the C ABI, against the fp64 oracle on the
 same seeded inputs: the pages' toy values on the plain fp32 kernel,
-DeepSeek-V2 width (k = 16384, d = 5120) on the MFMA kernels for 1..100
-rows, an odd shape on the plain bf16 kernel, and the projection of a real
+DeepSeek-V2 width (k = 16384, d = 5120) on the one-launch few-row kernel
+for 1..4 rows and on the MFMA kernels from 5 to 100 rows, an odd shape on the plain bf16 kernel, and the projection of a real
 decode step's output.
 
 Tolerance (normwise, as for the decode step): 1e-2 for a bf16 output, 1e-5
@@ -60,7 +60,7 @@ def test_p5_toy_output_projection(torch, which):
     np.testing.assert_allclose(got, src["u4"]["value"], rtol=0, atol=1e-6)
 
 
-@pytest.mark.parametrize("rows", [1, 3, 32, 64, 100])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 32, 64, 100])
 @pytest.mark.parametrize("out_dtype", ["bf16", "f32"])
 def test_deepseek_v2_width(torch, rows, out_dtype):
     case = inputs.make_oproj(rows, seed=300 + rows)
@@ -69,6 +69,20 @@ def test_deepseek_v2_width(torch, rows, out_dtype):
     ref = oracle.output_project(inputs.widen(case["o"], "bf16"), inputs.widen(case["w_o"], "bf16"))
     log("oproj rows=%d: %d slices of k" % (rows, binding.mla_oproj_workspace_size(rows, k, d) // max(1, rows * d * 4)))
     check(u.float().cpu().numpy().astype(np.float64), ref, out_dtype, "oproj rows=%d out=%s" % (rows, out_dtype))
+
+
+@pytest.mark.parametrize("rows,k", [(1, 16384), (1, 32768), (2, 16384), (3, 4096), (4, 4096)])
+def test_few_rows_one_launch(torch, rows, k):
+    """The one-launch few-row kernel in both of its forms: x read from L2
+    (one and two rows) and x staged in LDS (three and four rows of 4096);
+    d = 512."""
+    case = inputs.make_oproj(rows, h=k // 128, d_h=128, d_model=512, seed=330 + rows + k // 1024)
+    assert binding.mla_oproj_workspace_size(rows, k, 512) == 0  # no partials
+    for out_dtype in ("bf16", "f32"):
+        u, _, _ = _project(torch, case["o"], case["w_o"], "bf16", out_dtype, rows, k, 512)
+        ref = oracle.output_project(inputs.widen(case["o"], "bf16"), inputs.widen(case["w_o"], "bf16"))
+        check(u.float().cpu().numpy().astype(np.float64), ref, out_dtype,
+              "oproj few rows=%d k=%d out=%s" % (rows, k, out_dtype))
 
 
 def test_odd_shape_takes_the_plain_kernel(torch):

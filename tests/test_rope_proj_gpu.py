@@ -5,7 +5,8 @@ and the query side (query latent, content query, RoPE query).
 
 - The pages' toy on the plain fp32 kernels, against its printed values.
 - DeepSeek-V2 widths (d_model 5120, d_c 512, d_r 64, d_qc 1536, 128 heads of
-  128) on the MFMA path, with positions up to 131071 (fp64 angles).
+  128) on the one-launch few-row kernels (1..4 rows) and the MFMA path (5
+  rows and more), with positions up to 131071 (fp64 angles).
 - One whole step from hidden states: cache append, query side, decode and
   output projection on the GPU against the same chain in the oracle.
 
@@ -86,7 +87,7 @@ def _paged_layout(rng, seqs, max_pages, page_size):
     return rng.permutation(num_pages).reshape(seqs, max_pages).astype(np.int32), num_pages
 
 
-@pytest.mark.parametrize("rows", [1, 32, 64])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 32, 64])
 def test_cache_append_deepseek_v2(torch, rows):
     rng = np.random.default_rng(410 + rows)
     case = inputs.make_projections(rows, seed=420 + rows)
@@ -127,6 +128,30 @@ def test_cache_append_deepseek_v2(torch, rows):
     assert int((rp.view(-1, 64).abs().sum(1) != 0).sum()) == rows
 
 
+@pytest.mark.parametrize("rows,d_model", [(1, 24576), (2, 12288)])
+def test_cache_append_long_hidden_state(torch, rows, d_model):
+    """Hidden states longer than DeepSeek-V2's on the few-row kernel (x read
+    from L2 by every wave); contiguous pages, d_c 512, d_r 64."""
+    case = inputs.make_projections(rows, d_model=d_model, d_qc=512, h=1, d_h=128, seed=460 + rows)
+    assert binding.mla_cache_append_workspace_size(rows, d_model, 512, 64) == 0
+    page_size, max_pages = 64, 4
+    table = np.arange(2 * max_pages, dtype=np.int32).reshape(2, max_pages)
+    seq = np.arange(rows, dtype=np.int32) % 2
+    pos = np.array([200, 37][:rows], dtype=np.int32)
+    lat = torch.zeros((table.size, page_size, 512), dtype=torch.bfloat16, device="cuda")
+    rp = torch.zeros((table.size, page_size, 64), dtype=torch.bfloat16, device="cuda")
+    op = binding.CacheAppend(d_model, 512, 64, "bf16")
+    op.run(_dev(torch, case["x"], "bf16"), _dev(torch, case["w_dkv"], "bf16"), _dev(torch, case["w_kr"], "bf16"),
+           torch.from_numpy(seq).cuda(), torch.from_numpy(pos).cuda(), torch.from_numpy(table).cuda(), lat, rp)
+    torch.cuda.synchronize()
+    w = {k: inputs.widen(case[k], "bf16") for k in ("x", "w_dkv", "w_kr")}
+    ref_lat, ref_rp = oracle.cache_append(w["x"], w["w_dkv"], w["w_kr"], seq, pos, oracle.rope_thetas(64, 10000.0),
+                                          table, page_size, np.zeros((table.size, page_size, 512)),
+                                          np.zeros((table.size, page_size, 64)))
+    check(lat.float().cpu().numpy().astype(np.float64), ref_lat, "bf16", "cache append latent, d_model %d" % d_model)
+    check(rp.float().cpu().numpy().astype(np.float64), ref_rp, "bf16", "cache append RoPE key, d_model %d" % d_model)
+
+
 def test_cache_append_skips_rows_outside_the_table(torch):
     """A position past the table, or a page id outside the pool, writes
     nothing (the other rows are still written)."""
@@ -145,7 +170,7 @@ def test_cache_append_skips_rows_outside_the_table(torch):
     assert (rp.view(-1, 64).abs().sum(1) != 0).nonzero().flatten().tolist() == [5]
 
 
-@pytest.mark.parametrize("rows", [1, 16, 64])
+@pytest.mark.parametrize("rows", [1, 2, 3, 4, 5, 16, 64])
 def test_query_side_deepseek_v2(torch, rows):
     case = inputs.make_projections(rows, seed=440 + rows)
     pos = np.random.default_rng(450 + rows).integers(0, 131072, size=rows).astype(np.int32)

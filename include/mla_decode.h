@@ -212,8 +212,10 @@ mla_status_t mla_decode_read_timing_runs(mla_decode_t plan, float* ms, int32_t m
  *   workspace             mla_oproj_workspace_size bytes (fp32 partial sums
  *                          over slices of k; 0 bytes, and NULL allowed, when
  *                          it returns 0), 256-byte aligned, caller-owned
- * bf16 storage with d_model % 64 == 0 and k % 512 == 0 runs on MFMA with
- * fp32 accumulation (16-byte aligned o, w_o and u required); other shapes
+ * bf16 storage with d_model % 64 == 0 and k % 512 == 0 runs with fp32
+ * accumulation (16-byte aligned o, w_o and u required): up to four rows in
+ * one launch with bf16 dot products and no workspace (x within 40 KB for
+ * three or four rows), more rows on MFMA over slices of k; other shapes
  * and fp32 storage on a plain fp32 kernel.  The result does not depend on
  * timing (partials are summed in a fixed order).  Enqueued on `stream`
  * (a hipStream_t, NULL = the null stream); no allocation, no
@@ -247,8 +249,9 @@ mla_status_t mla_oproj_run(int32_t rows, int32_t k, int32_t d_model, int32_t dty
  *   workspace   mla_cache_append_workspace_size bytes (NULL when 0), 256-byte aligned
  * A row whose position or page lies outside the table or the pool is not
  * written.  bf16 with d_model % 512 == 0 and d_c, d_r multiples of 64 runs
- * on MFMA (16-byte aligned tensors); other shapes and fp32 on a plain
- * kernel.  Rows that write the same pool row race.  Enqueued on `stream`;
+ * the fast kernels (16-byte aligned tensors): up to four rows one launch
+ * with no workspace, more rows MFMA over slices of k; other shapes and
+ * fp32 on a plain kernel.  Rows that write the same pool row race.  Enqueued on `stream`;
  * no allocation, no synchronisation; argument errors return a negative
  * status before any launch. */
 size_t mla_cache_append_workspace_size(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t dtype);
@@ -274,8 +277,9 @@ mla_status_t mla_cache_append_run(int32_t rows, int32_t d_model, int32_t d_c, in
  *   (c_Q, kept in dtype -- bf16 rounds it to nearest even as the next
  *   product's operand -- and fp32 partial sums).
  * RoPE as for mla_cache_append_run.  bf16 with d_model and d_qc multiples of
- * 512 and d_qc, h * d_h, h * d_r multiples of 64 runs on MFMA; other shapes
- * and fp32 on plain kernels.  Enqueued on `stream`; no allocation, no
+ * 512 and d_qc, h * d_h, h * d_r multiples of 64 runs the fast kernels (one
+ * launch per stage up to four rows, MFMA over slices of k beyond); other
+ * shapes and fp32 on plain kernels.  Enqueued on `stream`; no allocation, no
  * synchronisation; argument errors return a negative status before any
  * launch. */
 size_t mla_query_project_workspace_size(int32_t rows, int32_t d_model, int32_t d_qc, int32_t h, int32_t d_h,

@@ -48,6 +48,7 @@ KERNELS = {
     "prefill_attn": ("prefill_attn", ("prefill.hip",)),
     "kv_rebuild": ("kv_rebuild", ("prefill.hip",)),
     "rope_finish": ("rope_finish", ("rope_proj.hip",)),
+    "rope_rows": ("rope_rows", ("rope_proj.hip",)),
 }
 
 

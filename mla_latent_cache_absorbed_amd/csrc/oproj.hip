@@ -150,17 +150,19 @@ __global__ __launch_bounds__(kThreads) void oproj_partial_kernel(OprojArgs a) {
   }
 }
 
-// Up to kR rows (rows_dot_applies): wave = output features n, n + 1 over the
-// whole of k; lane r stores row r.
-template <int kR, bool kLds, int kDepth>
+// Up to kR rows (rows_dot_applies): output features n, n + 1 over the whole
+// of k, by one wave or by the work-group's kSplit waves; lane r of the wave
+// with the sums stores row r.
+template <int kR, bool kLds, int kDepth, int kSplit>
 __global__ __launch_bounds__(kRowsDotWaves * 64) void oproj_rows_kernel(OprojArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t x_lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int n = kRowsDotFeatures * (blockIdx.x * kRowsDotWaves + wave);  // < d: the grid is d / 8
+  // < d: the grid is d / (8 / kSplit)
+  const int n = kRowsDotFeatures * (blockIdx.x * (kRowsDotWaves / kSplit) + wave / kSplit);
   const uint16_t* w = a.w + (size_t)n * a.k;
   float s[kRowsDotFeatures][kR];
-  rows_dot<kR, kLds, kDepth>(a.o, a.rows, a.k, w, w + a.k, x_lds, s);
+  if (!rows_dot<kR, kLds, kDepth, kSplit>(a.o, a.rows, a.k, w, w + a.k, x_lds, s, [] {})) return;
   if (lane >= a.rows) return;
   float v0, v1;
   rows_dot_pick<kR>(s, lane, v0, v1);
@@ -285,16 +287,26 @@ hipError_t launch_oproj(const OprojLaunch& p, const LaunchCtx& s) {
     a.splits = 1;
     a.out_bf16 = p.out_bf16;
     a.write_part = 0;
-    const dim3 grid(p.d / kRowsDotPerGroup), block(kRowsDotWaves * 64);
+    const int split = rows_dot_split(p.d, p.k);
+    const dim3 grid(p.d / (kRowsDotPerGroup / split)), block(kRowsDotWaves * 64);
     const size_t lds = rows_dot_lds_bytes(p.rows, p.k);
-    if (lds > 0)  // three or four rows of x, staged in LDS
-      launch_kernel_lds(oproj_rows_kernel<4, true, kRowsDotDepth>, grid, block, lds, s, a);
-    else if (rows_dot_deep(p.rows, p.k))  // one or two rows of x, read from L2
-      launch_kernel(oproj_rows_kernel<1, false, kRowsDotDeepDepth>, grid, block, s, a);
-    else if (p.rows == 1)
-      launch_kernel(oproj_rows_kernel<1, false, kRowsDotDepth>, grid, block, s, a);
-    else
-      launch_kernel(oproj_rows_kernel<2, false, kRowsDotDepth>, grid, block, s, a);
+    constexpr int kD = kRowsDotDepth, kW = kRowsDotWaves;
+    if (split > 1) {  // few features: the work-group's waves split k
+      if (lds > 0)
+        launch_kernel_lds(oproj_rows_kernel<4, true, kD, kW>, grid, block, lds, s, a);
+      else if (p.rows == 1)
+        launch_kernel(oproj_rows_kernel<1, false, kD, kW>, grid, block, s, a);
+      else
+        launch_kernel(oproj_rows_kernel<2, false, kD, kW>, grid, block, s, a);
+    } else if (lds > 0) {  // three or four rows of x, staged in LDS
+      launch_kernel_lds(oproj_rows_kernel<4, true, kD, 1>, grid, block, lds, s, a);
+    } else if (rows_dot_deep(p.rows, p.k)) {  // one or two rows of x, read from L2
+      launch_kernel(oproj_rows_kernel<1, false, kRowsDotDeepDepth, 1>, grid, block, s, a);
+    } else if (p.rows == 1) {
+      launch_kernel(oproj_rows_kernel<1, false, kD, 1>, grid, block, s, a);
+    } else {
+      launch_kernel(oproj_rows_kernel<2, false, kD, 1>, grid, block, s, a);
+    }
     return hipGetLastError();
   }
   const hipError_t e = launch_partial(p.o, p.w, nullptr, p.rows, p.k, p.d, p.d, static_cast<float*>(p.part), false,

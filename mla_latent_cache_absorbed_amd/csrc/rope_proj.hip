@@ -119,9 +119,10 @@ __global__ __launch_bounds__(kThreads) void rope_finish_kernel(FinishArgs a) {
   *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-// Up to kR rows: wave = output features n, n + 1 of the stacked weights
-// [w0; w1] over the whole of k (n even, so a RoPE pair stays in one wave);
-// lane r finishes row r.
+// Up to kR rows: output features n, n + 1 of the stacked weights [w0; w1]
+// over the whole of k (n even, so a RoPE pair stays together), by one wave
+// or by the work-group's kSplit waves; lane r of the wave with the sums
+// finishes row r.
 struct RowsArgs {
   const uint16_t* x;   // [rows][k]
   const uint16_t* w0;  // [n0][k]
@@ -133,33 +134,42 @@ struct RowsArgs {
   Dest dst;
 };
 
-template <int kR, bool kLds, int kDepth>
+template <int kR, bool kLds, int kDepth, int kSplit>
 __global__ __launch_bounds__(kRowsDotWaves * 64) void rope_rows_kernel(RowsArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t x_lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int n = kRowsDotFeatures * (blockIdx.x * kRowsDotWaves + wave);  // < n0 + n1: the grid is (n0 + n1) / 8
+  // < n0 + n1: the grid is (n0 + n1) / (8 / kSplit)
+  const int n = kRowsDotFeatures * (blockIdx.x * (kRowsDotWaves / kSplit) + wave / kSplit);
   const uint16_t* w = n < a.n0 ? a.w0 + (size_t)n * a.k : a.w1 + (size_t)(n - a.n0) * a.k;
+  // the row's position is loaded ahead of the weights, and a RoPE pair's
+  // angle (fp64 pow and sincos: ~1 us of latency) is worked out while the
+  // first weight loads are in flight
+  const int t = lane < a.rows ? a.pos[lane] : 0;
+  float c = 1.f, si = 0.f;
+  auto angle = [&] {
+    if (n >= a.n0 && lane < a.rows) {
+      double sn, cs;
+      sincos((double)t * rope_theta(a.theta, a.base, ((n - a.n0) % a.d_r) / 2, a.d_r), &sn, &cs);
+      c = (float)cs;
+      si = (float)sn;
+    }
+  };
   float sums[kRowsDotFeatures][kR];
-  rows_dot<kR, kLds, kDepth>(a.x, a.rows, a.k, w, w + a.k, x_lds, sums);
+  if (!rows_dot<kR, kLds, kDepth, kSplit>(a.x, a.rows, a.k, w, w + a.k, x_lds, sums, angle)) return;
   if (lane >= a.rows) return;
   float v0, v1;
   rows_dot_pick<kR>(sums, lane, v0, v1);
-  const int t = a.pos[lane];
   size_t row;
   if (!dest_row(a.dst, lane, t, row)) return;
   uint16_t* out;
   if (n < a.n0) {
     out = static_cast<uint16_t*>(a.dst.out0) + row * a.n0 + n;
   } else {
-    const int g = n - a.n0;
-    double sn, cs;
-    sincos((double)t * rope_theta(a.theta, a.base, (g % a.d_r) / 2, a.d_r), &sn, &cs);
-    const float c = (float)cs, si = (float)sn;
     const float x0 = v0, x1 = v1;
     v0 = x0 * c - x1 * si;
     v1 = x1 * c + x0 * si;
-    out = static_cast<uint16_t*>(a.dst.out1) + row * a.n1 + g;
+    out = static_cast<uint16_t*>(a.dst.out1) + row * a.n1 + (n - a.n0);
   }
   *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(v0, v1);
 }
@@ -218,16 +228,26 @@ hipError_t run_stage(const void* x, const void* w0, const void* w1, int rows, in
     a.theta = theta;
     a.base = base;
     a.dst = dst;
-    const dim3 grid((n0 + n1) / kRowsDotPerGroup), block(kRowsDotWaves * 64);
+    const int split = rows_dot_split(n0 + n1, k);
+    const dim3 grid((n0 + n1) / (kRowsDotPerGroup / split)), block(kRowsDotWaves * 64);
     const size_t lds = rows_dot_lds_bytes(rows, k);
-    if (lds > 0)  // three or four rows of x, staged in LDS
-      launch_kernel_lds(rope_rows_kernel<4, true, kRowsDotDepth>, grid, block, lds, s, a);
-    else if (rows_dot_deep(rows, k))  // one or two rows of x, read from L2
-      launch_kernel(rope_rows_kernel<1, false, kRowsDotDeepDepth>, grid, block, s, a);
-    else if (rows == 1)
-      launch_kernel(rope_rows_kernel<1, false, kRowsDotDepth>, grid, block, s, a);
-    else
-      launch_kernel(rope_rows_kernel<2, false, kRowsDotDepth>, grid, block, s, a);
+    constexpr int kD = kRowsDotDepth, kW = kRowsDotWaves;
+    if (split > 1) {  // few features: the work-group's waves split k
+      if (lds > 0)
+        launch_kernel_lds(rope_rows_kernel<4, true, kD, kW>, grid, block, lds, s, a);
+      else if (rows == 1)
+        launch_kernel(rope_rows_kernel<1, false, kD, kW>, grid, block, s, a);
+      else
+        launch_kernel(rope_rows_kernel<2, false, kD, kW>, grid, block, s, a);
+    } else if (lds > 0) {  // three or four rows of x, staged in LDS
+      launch_kernel_lds(rope_rows_kernel<4, true, kD, 1>, grid, block, lds, s, a);
+    } else if (rows_dot_deep(rows, k)) {  // one or two rows of x, read from L2
+      launch_kernel(rope_rows_kernel<1, false, kRowsDotDeepDepth, 1>, grid, block, s, a);
+    } else if (rows == 1) {
+      launch_kernel(rope_rows_kernel<1, false, kD, 1>, grid, block, s, a);
+    } else {
+      launch_kernel(rope_rows_kernel<2, false, kD, 1>, grid, block, s, a);
+    }
     return hipGetLastError();
   }
   if (fast) {

@@ -50,6 +50,15 @@ constexpr int kRowsDotPerGroup = kRowsDotWaves * kRowsDotFeatures;
 constexpr int kRowsDotDepth = 4;
 constexpr int kRowsDotDeepDepth = 8;
 __host__ __device__ inline bool rows_dot_deep(int rows, int k) { return rows == 1 && k >= 16 * kRowsDotK; }
+// Waves that share one feature pair, each taking every kSplit-th step of
+// k: 4 (the whole work-group) when the features are few (n < 1024: the
+// cache append's 576), so that a wave's chain of dependent loads is a
+// quarter as long; else 1.  The partial sums meet in LDS in wave order.
+// (Cache append at 2 and 4 rows: 10.6 -> 9.6 and 12.0 -> 10.9 us; the
+// query latent's 1536 features measured 0.5 us slower split.)
+__host__ __device__ inline int rows_dot_split(int n, int k) {
+  return n < 1024 && k / kRowsDotK >= kRowsDotWaves ? kRowsDotWaves : 1;
+}
 // Largest x a work-group holds in LDS (rows * k bf16 values): four
 // work-groups per CU.
 constexpr size_t kRowsDotMaxLdsBytes = 40 * 1024;
@@ -84,36 +93,48 @@ __device__ __forceinline__ float dot8_bf16(u32x4 a, u32x4 b, float c) {
 // out[f][r] = sum over k of wf[k] x[r][k] for the two feature rows w0, w1
 // (k contiguous values each) and the rows r < kR of x ([rows][k]); every
 // lane receives every sum.  A row r >= rows reads row 0 instead and its
-// sums are to be dropped.  kDepth: kRowsDotDeepDepth when rows_dot_deep,
-// else kRowsDotDepth.  kLds (= rows_dot_x_in_lds(rows, k)): called by
-// all threads of the work-group (kRowsDotWaves waves) with xs the
-// work-group's LDS of rows_dot_lds_bytes(rows, k) bytes; contains one
-// barrier.  Otherwise xs is unused and the waves run independently.
-template <int kR, bool kLds, int kDepth>
-__device__ __forceinline__ void rows_dot(const uint16_t* x, int rows, int k, const uint16_t* w0, const uint16_t* w1,
-                                         uint16_t* xs, float (&out)[kRowsDotFeatures][kR]) {
+// sums are to be dropped.  kDepth: kRowsDotDeepDepth when rows_dot_deep
+// (and kSplit is 1), else kRowsDotDepth.  kSplit = rows_dot_split(n, k):
+// the waves w with the same w / kSplit share w0, w1, wave w taking the
+// steps w % kSplit, w % kSplit + kSplit, ...; the return value says
+// whether this wave holds the finished sums (one wave per pair).  kLds
+// (= rows_dot_x_in_lds(rows, k)) or kSplit > 1: called by all threads of
+// the work-group (kRowsDotWaves waves), with xs the work-group's LDS of
+// rows_dot_lds_bytes(rows, k) bytes for kLds; one barrier for each.
+// Otherwise xs is unused and the waves run independently.  pre() runs once
+// the first steps' loads are out (work of the caller's epilogue that does
+// not depend on the sums).
+template <int kR, bool kLds, int kDepth, int kSplit, typename Pre>
+__device__ __forceinline__ bool rows_dot(const uint16_t* x, int rows, int k, const uint16_t* w0, const uint16_t* w1,
+                                         uint16_t* xs, float (&out)[kRowsDotFeatures][kR], Pre pre) {
+  static_assert(kSplit == 1 || kSplit == kRowsDotWaves, "a feature pair takes one wave or the whole work-group");
   const int lane = threadIdx.x & 63;
-  const int steps = k / kRowsDotK;
-  const uint16_t* wp[kRowsDotFeatures] = {w0 + 8 * lane, w1 + 8 * lane};
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = wave % kSplit;
+  const int steps = (k / kRowsDotK - part + kSplit - 1) / kSplit;  // this wave's steps (>= 1)
+  constexpr size_t kStride = (size_t)kRowsDotK * kSplit;           // elements between them
+  const int e0 = kRowsDotK * part + 8 * lane;
+  const uint16_t* wp[kRowsDotFeatures] = {w0 + e0, w1 + e0};
   const uint16_t* xg[kR];  // x rows in global memory (not kLds)
 #pragma unroll
-  for (int r = 0; r < kR; ++r) xg[r] = x + (size_t)(r < rows ? r : 0) * k + 8 * lane;
+  for (int r = 0; r < kR; ++r) xg[r] = x + (size_t)(r < rows ? r : 0) * k + e0;
 
   u32x4 wv[kDepth][kRowsDotFeatures];
   u32x4 xv[kLds ? 1 : kDepth][kR];
   auto load = [&](int slot, int s) {
 #pragma unroll
     for (int f = 0; f < kRowsDotFeatures; ++f)
-      wv[slot][f] = *reinterpret_cast<const u32x4*>(wp[f] + (size_t)kRowsDotK * s);
+      wv[slot][f] = *reinterpret_cast<const u32x4*>(wp[f] + kStride * s);
     if constexpr (!kLds) {
 #pragma unroll
-      for (int r = 0; r < kR; ++r) xv[slot][r] = *reinterpret_cast<const u32x4*>(xg[r] + (size_t)kRowsDotK * s);
+      for (int r = 0; r < kR; ++r) xv[slot][r] = *reinterpret_cast<const u32x4*>(xg[r] + kStride * s);
     }
   };
   // the first steps' loads go out before the copy of x (a step past the
   // end re-reads the last one: the loads stay unconditional)
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) load(u, u < steps ? u : steps - 1);
+  pre();  // the caller's work that does not need the sums, under those loads
 
   const uint16_t* xr[kR];  // x rows in LDS (kLds)
   if constexpr (kLds) {
@@ -122,7 +143,7 @@ __device__ __forceinline__ void rows_dot(const uint16_t* x, int rows, int k, con
       *reinterpret_cast<u32x4*>(xs + 8 * i) = *reinterpret_cast<const u32x4*>(x + 8 * (size_t)i);
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < kR; ++r) xr[r] = xs + (r < rows ? r : 0) * k + 8 * lane;
+    for (int r = 0; r < kR; ++r) xr[r] = xs + (r < rows ? r : 0) * k + e0;
   }
 
   float acc[kRowsDotFeatures][kR];
@@ -135,7 +156,7 @@ __device__ __forceinline__ void rows_dot(const uint16_t* x, int rows, int k, con
 #pragma unroll
     for (int r = 0; r < kR; ++r) {
       if constexpr (kLds)
-        xs_v[r] = *reinterpret_cast<const u32x4*>(xr[r] + kRowsDotK * s);
+        xs_v[r] = *reinterpret_cast<const u32x4*>(xr[r] + kStride * s);
       else
         xs_v[r] = xv[slot][r];
     }
@@ -171,6 +192,27 @@ __device__ __forceinline__ void rows_dot(const uint16_t* x, int rows, int k, con
       for (int m = 32; m >= 1; m >>= 1) v = xor_sum(v, m);
       out[f][r] = v;
     }
+  if constexpr (kSplit > 1) {
+    __shared__ float red[kRowsDotWaves][kRowsDotFeatures][kR];
+    if (lane == 0) {
+#pragma unroll
+      for (int f = 0; f < kRowsDotFeatures; ++f)
+#pragma unroll
+        for (int r = 0; r < kR; ++r) red[wave][f][r] = out[f][r];
+    }
+    __syncthreads();
+    if (part != 0) return false;
+#pragma unroll
+    for (int f = 0; f < kRowsDotFeatures; ++f)
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        float v = red[wave][f][r];
+#pragma unroll
+        for (int j = 1; j < kSplit; ++j) v += red[wave + j][f][r];
+        out[f][r] = v;
+      }
+  }
+  return true;
 }
 
 // The sums of row `lane` (lanes 0 .. kR - 1), for the lane that stores it.

@@ -323,9 +323,10 @@ def measure_oproj(rows, runs, warmup):
 def measure_projections(rows, runs, warmup):
     """The current token's projections at DeepSeek-V2 widths (d_model 5120,
     d_c 512, d_r 64, d_qc 1536, 128 heads of 128) for `rows` new tokens: the
-    cache append (into a 512-page pool) and the query side, each timed per
-    call with events on the launch stream over `runs` calls, rotating over
-    enough device copies of its weights to exceed 1 GiB."""
+    cache append (into a 512-page pool), the query side, and both in one
+    call (mla_token_project_run), each timed per call with events on the
+    launch stream over `runs` calls, rotating over enough device copies of
+    its weights to exceed 1 GiB."""
     import torch
     from mla_latent_cache_absorbed_amd import binding, inputs
     case = inputs.make_projections(rows, seed=480 + rows)
@@ -398,6 +399,25 @@ def measure_projections(rows, runs, warmup):
     out["query_project"] = record(t, w_bytes + rows * d_model * 2 + rows * h * (d_h + d_r) * 2,
                                   2 * rows * (d_qc * d_model + h * (d_h + d_r) * d_qc), n)
     del ws
+    # both in one call (mla_token_project_run): the same rows, positions and
+    # pools as the cache append above
+    lat = torch.zeros((pages, page_size, d_c), dtype=torch.bfloat16, device="cuda")
+    rp = torch.zeros((pages, page_size, d_r), dtype=torch.bfloat16, device="cuda")
+    w_bytes = ((d_c + d_r + d_qc) * d_model + h * (d_h + d_r) * d_qc) * 2
+    n = max(2, math.ceil(MIN_ROTATION_BYTES / w_bytes))
+    w0 = tuple(dev(case[k]) for k in ("w_dkv", "w_kr", "w_dq", "w_uq", "w_qr"))
+    ws = [w0] + [tuple(w.clone() for w in w0) for _ in range(n - 1)]
+    need = binding.mla_token_project_workspace_size(rows, d_model, d_c, d_r, d_qc, h, d_h)
+    work = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    calls = [(rows, d_model, d_c, d_r, d_qc, h, d_h, binding.MLA_DTYPE_BF16, x.data_ptr()) +
+             tuple(w.data_ptr() for w in ww) +
+             (seq.data_ptr(), pos.data_ptr(), table.data_ptr(), pages, page_size, pages, lat.data_ptr(),
+              rp.data_ptr(), q.data_ptr(), q_r.data_ptr(), None, 10000.0, work.data_ptr(), need, stream)
+             for ww in ws]
+    t = timed(calls, L.mla_token_project_run)
+    out["token_project"] = record(t, w_bytes + rows * d_model * 2 + rows * (d_c + d_r + h * (d_h + d_r)) * 2,
+                                  2 * rows * ((d_c + d_r + d_qc) * d_model + h * (d_h + d_r) * d_qc), n)
+    del ws, lat, rp
     return out
 
 

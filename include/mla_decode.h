@@ -290,6 +290,32 @@ mla_status_t mla_query_project_run(int32_t rows, int32_t d_model, int32_t d_qc, 
                                    void* q_r, const double* rope_theta, double rope_base, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* Both projections of the current tokens in one call: the cache append of
+ * mla_cache_append_run and the query side of mla_query_project_run for
+ * the same rows, hidden states x and positions pos (the latent, the RoPE
+ * key and the query latent all read x: "Multi-Head Latent Attention: ...",
+ * sections "MLA: Low-Rank Key-Value Joint Compression" and on the query
+ * compression; "MLA, dim by dim" sections 4.3 and 5.2).  Arguments as in
+ * those two calls (one rope_theta / rope_base for keys and queries);
+ * workspace mla_token_project_workspace_size bytes, 256-byte aligned.  Up
+ * to four rows of bf16 with the fast shapes, the first stages share one
+ * launch ([W_DKV; W_KR; W_DQ] x) and the call makes two launches in all;
+ * otherwise it runs the two calls in turn, with the same results.  Rows
+ * whose page lies outside the table or the pool are not written to the
+ * pools; their queries are.  Enqueued on `stream`; no allocation, no
+ * synchronisation; argument errors return a negative status before any
+ * launch. */
+size_t mla_token_project_workspace_size(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t d_qc,
+                                        int32_t h, int32_t d_h, int32_t dtype);
+mla_status_t mla_token_project_run(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t d_qc,
+                                   int32_t h, int32_t d_h, int32_t dtype, const void* x, const void* w_dkv,
+                                   const void* w_kr, const void* w_dq, const void* w_uq, const void* w_qr,
+                                   const int32_t* seq, const int32_t* pos, const int32_t* page_table,
+                                   int32_t max_pages_per_seq, int32_t page_size, int32_t num_pages,
+                                   void* latent_pool, void* rope_pool, void* q, void* q_r,
+                                   const double* rope_theta, double rope_base, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* Prefill: attention over a whole prompt of T tokens, each attending to
  * itself and the tokens before it, in the order the pages derive for many
  * queries ("MLA, dim by dim" section 4.1): the per-head keys and values are

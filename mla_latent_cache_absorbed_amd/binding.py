@@ -33,6 +33,7 @@ EXPORTED = ("mla_decode_create", "mla_decode_workspace_size", "mla_decode_split_
             "mla_decode_last_error", "mla_oproj_workspace_size", "mla_oproj_run",
             "mla_cache_append_workspace_size", "mla_cache_append_run",
             "mla_query_project_workspace_size", "mla_query_project_run",
+            "mla_token_project_workspace_size", "mla_token_project_run",
             "mla_prefill_workspace_size", "mla_prefill_run")
 
 KERNELS = ("q_absorb", "split_attn", "combine", "up_project")
@@ -99,6 +100,10 @@ def lib():
         L.mla_query_project_workspace_size.restype = sz
         L.mla_query_project_run.argtypes = [i32] * 7 + [vp] * 8 + [dbl, vp, sz, vp]
         L.mla_query_project_run.restype = ctypes.c_int
+        L.mla_token_project_workspace_size.argtypes = [i32] * 8
+        L.mla_token_project_workspace_size.restype = sz
+        L.mla_token_project_run.argtypes = [i32] * 8 + [vp] * 9 + [i32] * 3 + [vp] * 5 + [dbl, vp, sz, vp]
+        L.mla_token_project_run.restype = ctypes.c_int
         L.mla_prefill_workspace_size.argtypes = [i32] * 4
         L.mla_prefill_workspace_size.restype = sz
         L.mla_prefill_run.argtypes = [i32] * 7 + [ctypes.c_float] + [vp] * 8 + [sz, vp]
@@ -315,6 +320,25 @@ def mla_query_project_run(rows, d_model, d_qc, h, d_h, d_r, x, w_dq, w_uq, w_qr,
         rows, d_model, d_qc, h, d_h, d_r, _DTYPE[dtype], _ptr(x), _ptr(w_dq), _ptr(w_uq), _ptr(w_qr), _ptr(pos),
         _ptr(q), _ptr(q_r), _ptr(rope_theta), float(rope_base), _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def mla_token_project_workspace_size(rows, d_model, d_c, d_r, d_qc, h, d_h, dtype="bf16") -> int:
+    return int(lib().mla_token_project_workspace_size(rows, d_model, d_c, d_r, d_qc, h, d_h, _DTYPE[dtype]))
+
+
+def mla_token_project_run(rows, d_model, d_c, d_r, d_qc, h, d_h, x, w_dkv, w_kr, w_dq, w_uq, w_qr, seq, pos,
+                          page_table, max_pages_per_seq, page_size, num_pages, latent_pool, rope_pool, q, q_r,
+                          rope_theta=None, rope_base=10000.0, workspace=None, workspace_bytes=None, dtype="bf16",
+                          stream=None) -> int:
+    """The cache append and the query side of the same rows in one call
+    (tensors or raw device addresses)."""
+    if workspace_bytes is None:
+        workspace_bytes = _nbytes(workspace)
+    return _check(lib().mla_token_project_run(
+        rows, d_model, d_c, d_r, d_qc, h, d_h, _DTYPE[dtype], _ptr(x), _ptr(w_dkv), _ptr(w_kr), _ptr(w_dq),
+        _ptr(w_uq), _ptr(w_qr), _ptr(seq), _ptr(pos), _ptr(page_table), max_pages_per_seq, page_size, num_pages,
+        _ptr(latent_pool), _ptr(rope_pool), _ptr(q), _ptr(q_r), _ptr(rope_theta), float(rope_base), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
 
 
 def _device_workspace(nbytes, device):

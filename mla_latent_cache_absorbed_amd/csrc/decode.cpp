@@ -323,6 +323,108 @@ mla_status_t oproj_check(int32_t rows, int32_t k, int32_t d_model, int32_t dtype
   return MLA_OK;
 }
 
+// Argument checks of the cache append (shapes before the rows == 0 exit,
+// then pointers), shared by mla_cache_append_run and mla_token_project_run.
+mla_status_t append_shape_check(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t dtype,
+                                int32_t max_pages_per_seq, int32_t page_size, int32_t num_pages,
+                                const double* rope_theta, double rope_base) {
+  if (rows < 0 || d_model < 1 || d_c < 1 || d_r < 2 || d_r % 2 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "rows >= 0, d_model, d_c >= 1 and an even d_r >= 2 are required");
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (max_pages_per_seq < 1 || page_size < 1 || num_pages < 1)
+    return fail(MLA_ERR_INVALID_ARG, "max_pages_per_seq, page_size and num_pages must be >= 1");
+  if (!rope_theta && !(rope_base > 1.0))
+    return fail(MLA_ERR_INVALID_ARG, "rope_base must be > 1 when no rope_theta is given");
+  return MLA_OK;
+}
+
+mla_status_t append_fill(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t dtype, const void* x,
+                         const void* w_dkv, const void* w_kr, const int32_t* seq, const int32_t* pos,
+                         const int32_t* page_table, int32_t max_pages_per_seq, int32_t page_size, int32_t num_pages,
+                         void* latent_pool, void* rope_pool, const double* rope_theta, double rope_base,
+                         void* workspace, mla::AppendLaunch& p) {
+  if (!x || !w_dkv || !w_kr || !seq || !pos || !page_table || !latent_pool || !rope_pool)
+    return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const size_t al = mla::cache_append_fast(d_model, d_c, d_r, bf16) ? 16 : (bf16 ? 2 : 4);
+  const void* vec[] = {x, w_dkv, w_kr, latent_pool, rope_pool};
+  for (const void* v : vec)
+    if (!aligned(v, al)) return fail(MLA_ERR_INVALID_ARG, "misaligned tensor (%zu-byte alignment needed)", al);
+  if (!aligned(seq, 4) || !aligned(pos, 4) || !aligned(page_table, 4) || (rope_theta && !aligned(rope_theta, 8)))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned index or frequency array");
+  p.x = x;
+  p.w_dkv = w_dkv;
+  p.w_kr = w_kr;
+  p.rows = rows;
+  p.d_model = d_model;
+  p.d_c = d_c;
+  p.d_r = d_r;
+  p.seq = seq;
+  p.pos = pos;
+  p.page_table = page_table;
+  p.max_pages = max_pages_per_seq;
+  p.page_size = page_size;
+  p.num_pages = num_pages;
+  p.latent_pool = latent_pool;
+  p.rope_pool = rope_pool;
+  p.theta = rope_theta;
+  p.base = rope_base;
+  p.bf16 = bf16;
+  p.work = workspace;
+  return MLA_OK;
+}
+
+// The same for the query side.
+mla_status_t query_shape_check(int32_t rows, int32_t d_model, int32_t d_qc, int32_t h, int32_t d_h, int32_t d_r,
+                               int32_t dtype, const double* rope_theta, double rope_base) {
+  if (rows < 0 || d_model < 1 || d_qc < 1 || h < 1 || d_h < 1 || d_r < 2 || d_r % 2 != 0)
+    return fail(MLA_ERR_INVALID_ARG, "rows >= 0, d_model, d_qc, h, d_h >= 1 and an even d_r >= 2 are required");
+  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!rope_theta && !(rope_base > 1.0))
+    return fail(MLA_ERR_INVALID_ARG, "rope_base must be > 1 when no rope_theta is given");
+  return MLA_OK;
+}
+
+mla_status_t query_fill(int32_t rows, int32_t d_model, int32_t d_qc, int32_t h, int32_t d_h, int32_t d_r,
+                        int32_t dtype, const void* x, const void* w_dq, const void* w_uq, const void* w_qr,
+                        const int32_t* pos, void* q, void* q_r, const double* rope_theta, double rope_base,
+                        void* workspace, mla::QueryLaunch& p) {
+  if (!x || !w_dq || !w_uq || !w_qr || !pos || !q || !q_r)
+    return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const size_t al = bf16 ? 16 : 4;
+  const void* vec[] = {x, w_dq, w_uq, w_qr, q, q_r};
+  for (const void* v : vec)
+    if (!aligned(v, al)) return fail(MLA_ERR_INVALID_ARG, "misaligned tensor (%zu-byte alignment needed)", al);
+  if (!aligned(pos, 4) || (rope_theta && !aligned(rope_theta, 8)))
+    return fail(MLA_ERR_INVALID_ARG, "misaligned position or frequency array");
+  p.x = x;
+  p.w_dq = w_dq;
+  p.w_uq = w_uq;
+  p.w_qr = w_qr;
+  p.rows = rows;
+  p.d_model = d_model;
+  p.d_qc = d_qc;
+  p.h = h;
+  p.d_h = d_h;
+  p.d_r = d_r;
+  p.pos = pos;
+  p.q = q;
+  p.q_r = q_r;
+  p.theta = rope_theta;
+  p.base = rope_base;
+  p.bf16 = bf16;
+  p.work = workspace;
+  return MLA_OK;
+}
+
+mla_status_t workspace_check(void* workspace, size_t workspace_bytes, size_t need) {
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
+  if (need > 0 && !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -484,47 +586,17 @@ mla_status_t mla_cache_append_run(int32_t rows, int32_t d_model, int32_t d_c, in
                                   const double* rope_theta, double rope_base, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (rows < 0 || d_model < 1 || d_c < 1 || d_r < 2 || d_r % 2 != 0)
-    return fail(MLA_ERR_INVALID_ARG, "rows >= 0, d_model, d_c >= 1 and an even d_r >= 2 are required");
-  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (max_pages_per_seq < 1 || page_size < 1 || num_pages < 1)
-    return fail(MLA_ERR_INVALID_ARG, "max_pages_per_seq, page_size and num_pages must be >= 1");
-  if (!rope_theta && !(rope_base > 1.0))
-    return fail(MLA_ERR_INVALID_ARG, "rope_base must be > 1 when no rope_theta is given");
+  mla_status_t st = append_shape_check(rows, d_model, d_c, d_r, dtype, max_pages_per_seq, page_size, num_pages,
+                                       rope_theta, rope_base);
+  if (st != MLA_OK) return st;
   if (rows == 0) return MLA_OK;
-  if (!x || !w_dkv || !w_kr || !seq || !pos || !page_table || !latent_pool || !rope_pool)
-    return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
-  const bool bf16 = dtype == MLA_DTYPE_BF16;
-  const size_t need = mla::cache_append_workspace_bytes(rows, d_model, d_c, d_r, bf16);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
-  if (need > 0 && !aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t al = mla::cache_append_fast(d_model, d_c, d_r, bf16) ? 16 : (bf16 ? 2 : 4);
-  const void* vec[] = {x, w_dkv, w_kr, latent_pool, rope_pool};
-  for (const void* v : vec)
-    if (!aligned(v, al)) return fail(MLA_ERR_INVALID_ARG, "misaligned tensor (%zu-byte alignment needed)", al);
-  if (!aligned(seq, 4) || !aligned(pos, 4) || !aligned(page_table, 4) || (rope_theta && !aligned(rope_theta, 8)))
-    return fail(MLA_ERR_INVALID_ARG, "misaligned index or frequency array");
   mla::AppendLaunch p;
-  p.x = x;
-  p.w_dkv = w_dkv;
-  p.w_kr = w_kr;
-  p.rows = rows;
-  p.d_model = d_model;
-  p.d_c = d_c;
-  p.d_r = d_r;
-  p.seq = seq;
-  p.pos = pos;
-  p.page_table = page_table;
-  p.max_pages = max_pages_per_seq;
-  p.page_size = page_size;
-  p.num_pages = num_pages;
-  p.latent_pool = latent_pool;
-  p.rope_pool = rope_pool;
-  p.theta = rope_theta;
-  p.base = rope_base;
-  p.bf16 = bf16;
-  p.work = workspace;
+  st = append_fill(rows, d_model, d_c, d_r, dtype, x, w_dkv, w_kr, seq, pos, page_table, max_pages_per_seq,
+                   page_size, num_pages, latent_pool, rope_pool, rope_theta, rope_base, workspace, p);
+  if (st != MLA_OK) return st;
+  st = workspace_check(workspace, workspace_bytes,
+                       mla::cache_append_workspace_bytes(rows, d_model, d_c, d_r, dtype == MLA_DTYPE_BF16));
+  if (st != MLA_OK) return st;
   mla::LaunchCtx lc;
   lc.stream = static_cast<hipStream_t>(stream);
   const hipError_t e = mla::launch_cache_append(p, lc);
@@ -549,45 +621,65 @@ mla_status_t mla_query_project_run(int32_t rows, int32_t d_model, int32_t d_qc, 
                                    const double* rope_theta, double rope_base, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   g_last_error.clear();
-  if (rows < 0 || d_model < 1 || d_qc < 1 || h < 1 || d_h < 1 || d_r < 2 || d_r % 2 != 0)
-    return fail(MLA_ERR_INVALID_ARG, "rows >= 0, d_model, d_qc, h, d_h >= 1 and an even d_r >= 2 are required");
-  if (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32) return fail(MLA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if (!rope_theta && !(rope_base > 1.0))
-    return fail(MLA_ERR_INVALID_ARG, "rope_base must be > 1 when no rope_theta is given");
+  mla_status_t st = query_shape_check(rows, d_model, d_qc, h, d_h, d_r, dtype, rope_theta, rope_base);
+  if (st != MLA_OK) return st;
   if (rows == 0) return MLA_OK;
-  if (!x || !w_dq || !w_uq || !w_qr || !pos || !q || !q_r || !workspace)
-    return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
-  const bool bf16 = dtype == MLA_DTYPE_BF16;
-  const size_t need = mla::query_project_workspace_bytes(rows, d_model, d_qc, h, d_h, d_r, bf16);
-  if (workspace_bytes < need) return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  if (!aligned(workspace, 256)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const size_t al = bf16 ? 16 : 4;
-  const void* vec[] = {x, w_dq, w_uq, w_qr, q, q_r};
-  for (const void* v : vec)
-    if (!aligned(v, al)) return fail(MLA_ERR_INVALID_ARG, "misaligned tensor (%zu-byte alignment needed)", al);
-  if (!aligned(pos, 4) || (rope_theta && !aligned(rope_theta, 8)))
-    return fail(MLA_ERR_INVALID_ARG, "misaligned position or frequency array");
   mla::QueryLaunch p;
-  p.x = x;
-  p.w_dq = w_dq;
-  p.w_uq = w_uq;
-  p.w_qr = w_qr;
-  p.rows = rows;
-  p.d_model = d_model;
-  p.d_qc = d_qc;
-  p.h = h;
-  p.d_h = d_h;
-  p.d_r = d_r;
-  p.pos = pos;
-  p.q = q;
-  p.q_r = q_r;
-  p.theta = rope_theta;
-  p.base = rope_base;
-  p.bf16 = bf16;
-  p.work = workspace;
+  st = query_fill(rows, d_model, d_qc, h, d_h, d_r, dtype, x, w_dq, w_uq, w_qr, pos, q, q_r, rope_theta, rope_base,
+                  workspace, p);
+  if (st != MLA_OK) return st;
+  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  st = workspace_check(workspace, workspace_bytes,
+                       mla::query_project_workspace_bytes(rows, d_model, d_qc, h, d_h, d_r, dtype == MLA_DTYPE_BF16));
+  if (st != MLA_OK) return st;
   mla::LaunchCtx lc;
   lc.stream = static_cast<hipStream_t>(stream);
   const hipError_t e = mla::launch_query_project(p, lc);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MLA_OK;
+}
+
+size_t mla_token_project_workspace_size(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t d_qc,
+                                        int32_t h, int32_t d_h, int32_t dtype) {
+  g_last_error.clear();
+  if (rows < 0 || d_model < 1 || d_c < 1 || d_qc < 1 || h < 1 || d_h < 1 || d_r < 2 || d_r % 2 != 0 ||
+      (dtype != MLA_DTYPE_BF16 && dtype != MLA_DTYPE_F32)) {
+    fail(MLA_ERR_INVALID_ARG, "bad token-projection shape or dtype");
+    return 0;
+  }
+  return mla::token_project_workspace_bytes(rows, d_model, d_c, d_r, d_qc, h, d_h, dtype == MLA_DTYPE_BF16);
+}
+
+mla_status_t mla_token_project_run(int32_t rows, int32_t d_model, int32_t d_c, int32_t d_r, int32_t d_qc,
+                                   int32_t h, int32_t d_h, int32_t dtype, const void* x, const void* w_dkv,
+                                   const void* w_kr, const void* w_dq, const void* w_uq, const void* w_qr,
+                                   const int32_t* seq, const int32_t* pos, const int32_t* page_table,
+                                   int32_t max_pages_per_seq, int32_t page_size, int32_t num_pages,
+                                   void* latent_pool, void* rope_pool, void* q, void* q_r,
+                                   const double* rope_theta, double rope_base, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  mla_status_t st = append_shape_check(rows, d_model, d_c, d_r, dtype, max_pages_per_seq, page_size, num_pages,
+                                       rope_theta, rope_base);
+  if (st == MLA_OK) st = query_shape_check(rows, d_model, d_qc, h, d_h, d_r, dtype, rope_theta, rope_base);
+  if (st != MLA_OK) return st;
+  if (rows == 0) return MLA_OK;
+  mla::AppendLaunch ap;
+  mla::QueryLaunch qp;
+  st = append_fill(rows, d_model, d_c, d_r, dtype, x, w_dkv, w_kr, seq, pos, page_table, max_pages_per_seq,
+                   page_size, num_pages, latent_pool, rope_pool, rope_theta, rope_base, workspace, ap);
+  if (st == MLA_OK)
+    st = query_fill(rows, d_model, d_qc, h, d_h, d_r, dtype, x, w_dq, w_uq, w_qr, pos, q, q_r, rope_theta, rope_base,
+                    workspace, qp);
+  if (st != MLA_OK) return st;
+  if (!workspace) return fail(MLA_ERR_INVALID_ARG, "a required device pointer is NULL");
+  st = workspace_check(workspace, workspace_bytes,
+                       mla::token_project_workspace_bytes(rows, d_model, d_c, d_r, d_qc, h, d_h,
+                                                          dtype == MLA_DTYPE_BF16));
+  if (st != MLA_OK) return st;
+  mla::LaunchCtx lc;
+  lc.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = mla::launch_token_project(ap, qp, lc);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return MLA_OK;
 }

@@ -156,6 +156,14 @@ struct QueryLaunch {
 size_t query_project_workspace_bytes(int rows, int d_model, int d_qc, int h, int d_h, int d_r, bool bf16);
 hipError_t launch_query_project(const QueryLaunch& p, const LaunchCtx& s);
 
+// The cache append and the query side of the same rows (rope_proj.hip; x,
+// rows, pos, theta and the workspace are the same in both): up to four
+// rows the first stages share one launch, [W_DKV; W_KR; W_DQ] x, so that x
+// and the launch are paid once; otherwise the two calls in turn.
+bool token_project_fused(int rows, int d_model, int d_c, int d_r, int d_qc, int h, int d_h, bool bf16);
+size_t token_project_workspace_bytes(int rows, int d_model, int d_c, int d_r, int d_qc, int h, int d_h, bool bf16);
+hipError_t launch_token_project(const AppendLaunch& ap, const QueryLaunch& qp, const LaunchCtx& s);
+
 // Prefill attention over a prompt of T tokens (prefill.hip): K and V rebuilt
 // from the latents, then causal attention over d_h + d_r dims.
 struct PrefillLaunch {

@@ -119,19 +119,24 @@ __global__ __launch_bounds__(kThreads) void rope_finish_kernel(FinishArgs a) {
   *reinterpret_cast<u32x2*>(out) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
 }
 
-// Up to kR rows: output features n, n + 1 of the stacked weights [w0; w1]
-// over the whole of k (n even, so a RoPE pair stays together), by one wave
-// or by the work-group's kSplit waves; lane r of the wave with the sums
-// finishes row r.
+// Up to kR rows: output features n, n + 1 of the stacked weights
+// [w0; w1; w2] over the whole of k (n even, so a RoPE pair stays together),
+// by one wave or by the work-group's kSplit waves; lane r of the wave with
+// the sums finishes row r.  w0 and w1 go to the destination (RoPE on w1);
+// w2, when n2 > 0, goes plainly to a dense [rows][n2] output (the query
+// latent when the cache append and the query side's first stage share one
+// launch).
 struct RowsArgs {
   const uint16_t* x;   // [rows][k]
   const uint16_t* w0;  // [n0][k]
   const uint16_t* w1;  // [n1][k]
-  int rows, k, n0, n1, d_r;
+  const uint16_t* w2;  // [n2][k]
+  int rows, k, n0, n1, n2, d_r;
   const int32_t* pos;
   const double* theta;
   double base;
   Dest dst;
+  uint16_t* out2;      // [rows][n2]
 };
 
 template <int kR, bool kLds, int kDepth, int kSplit>
@@ -139,16 +144,19 @@ __global__ __launch_bounds__(kRowsDotWaves * 64) void rope_rows_kernel(RowsArgs 
   extern __shared__ __attribute__((aligned(16))) uint16_t x_lds[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  // < n0 + n1: the grid is (n0 + n1) / (8 / kSplit)
+  // < n0 + n1 + n2: the grid is (n0 + n1 + n2) / (8 / kSplit)
   const int n = kRowsDotFeatures * (blockIdx.x * (kRowsDotWaves / kSplit) + wave / kSplit);
-  const uint16_t* w = n < a.n0 ? a.w0 + (size_t)n * a.k : a.w1 + (size_t)(n - a.n0) * a.k;
+  const int n01 = a.n0 + a.n1;
+  const uint16_t* w = n < a.n0 ? a.w0 + (size_t)n * a.k
+                      : n < n01 ? a.w1 + (size_t)(n - a.n0) * a.k
+                                : a.w2 + (size_t)(n - n01) * a.k;
   // the row's position is loaded ahead of the weights, and a RoPE pair's
   // angle (fp64 pow and sincos: ~1 us of latency) is worked out while the
   // first weight loads are in flight
   const int t = lane < a.rows ? a.pos[lane] : 0;
   float c = 1.f, si = 0.f;
   auto angle = [&] {
-    if (n >= a.n0 && lane < a.rows) {
+    if (n >= a.n0 && n < n01 && lane < a.rows) {
       double sn, cs;
       sincos((double)t * rope_theta(a.theta, a.base, ((n - a.n0) % a.d_r) / 2, a.d_r), &sn, &cs);
       c = (float)cs;
@@ -160,6 +168,10 @@ __global__ __launch_bounds__(kRowsDotWaves * 64) void rope_rows_kernel(RowsArgs 
   if (lane >= a.rows) return;
   float v0, v1;
   rows_dot_pick<kR>(sums, lane, v0, v1);
+  if (n >= n01) {  // the third weight: plain, dense rows
+    *reinterpret_cast<uint32_t*>(a.out2 + (size_t)lane * a.n2 + (n - n01)) = pack_bf16x2(v0, v1);
+    return;
+  }
   size_t row;
   if (!dest_row(a.dst, lane, t, row)) return;
   uint16_t* out;
@@ -209,47 +221,56 @@ __global__ __launch_bounds__(kThreads) void proj_rope_general_kernel(const T* x,
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// One projection stage with RoPE on the second weight: MFMA partials plus
-// the finish kernel, or the plain kernel.
+// The few-row kernel on [w0; w1; w2] (w2 optional: n2 = 0).
+hipError_t launch_rows(const void* x, const void* w0, const void* w1, const void* w2, int rows, int k, int n0, int n1,
+                       int n2, int d_r, const int32_t* pos, const double* theta, double base, const Dest& dst,
+                       void* out2, const LaunchCtx& s) {
+  RowsArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w0 = static_cast<const uint16_t*>(w0);
+  a.w1 = static_cast<const uint16_t*>(w1);
+  a.w2 = static_cast<const uint16_t*>(w2);
+  a.rows = rows;
+  a.k = k;
+  a.n0 = n0;
+  a.n1 = n1;
+  a.n2 = n2;
+  a.d_r = d_r;
+  a.pos = pos;
+  a.theta = theta;
+  a.base = base;
+  a.dst = dst;
+  a.out2 = static_cast<uint16_t*>(out2);
+  const int split = rows_dot_split(n0 + n1 + n2, k);
+  const dim3 grid((n0 + n1 + n2) / (kRowsDotPerGroup / split)), block(kRowsDotWaves * 64);
+  const size_t lds = rows_dot_lds_bytes(rows, k);
+  constexpr int kD = kRowsDotDepth, kW = kRowsDotWaves;
+  if (split > 1) {  // few features: the work-group's waves split k
+    if (lds > 0)
+      launch_kernel_lds(rope_rows_kernel<4, true, kD, kW>, grid, block, lds, s, a);
+    else if (rows == 1)
+      launch_kernel(rope_rows_kernel<1, false, kD, kW>, grid, block, s, a);
+    else
+      launch_kernel(rope_rows_kernel<2, false, kD, kW>, grid, block, s, a);
+  } else if (lds > 0) {  // three or four rows of x, staged in LDS
+    launch_kernel_lds(rope_rows_kernel<4, true, kD, 1>, grid, block, lds, s, a);
+  } else if (rows_dot_deep(rows, k)) {  // one or two rows of x, read from L2
+    launch_kernel(rope_rows_kernel<1, false, kRowsDotDeepDepth, 1>, grid, block, s, a);
+  } else if (rows == 1) {
+    launch_kernel(rope_rows_kernel<1, false, kD, 1>, grid, block, s, a);
+  } else {
+    launch_kernel(rope_rows_kernel<2, false, kD, 1>, grid, block, s, a);
+  }
+  return hipGetLastError();
+}
+
+// One projection stage with RoPE on the second weight: the few-row kernel,
+// or MFMA partials plus the finish kernel, or the plain kernel.
 hipError_t run_stage(const void* x, const void* w0, const void* w1, int rows, int k, int n0, int n1, int d_r,
                      const int32_t* pos, const double* theta, double base, const Dest& dst, bool bf16, bool fast,
                      float* part, const LaunchCtx& s) {
-  if (fast && rows_dot_applies(rows, k, n0 + n1)) {
-    RowsArgs a;
-    a.x = static_cast<const uint16_t*>(x);
-    a.w0 = static_cast<const uint16_t*>(w0);
-    a.w1 = static_cast<const uint16_t*>(w1);
-    a.rows = rows;
-    a.k = k;
-    a.n0 = n0;
-    a.n1 = n1;
-    a.d_r = d_r;
-    a.pos = pos;
-    a.theta = theta;
-    a.base = base;
-    a.dst = dst;
-    const int split = rows_dot_split(n0 + n1, k);
-    const dim3 grid((n0 + n1) / (kRowsDotPerGroup / split)), block(kRowsDotWaves * 64);
-    const size_t lds = rows_dot_lds_bytes(rows, k);
-    constexpr int kD = kRowsDotDepth, kW = kRowsDotWaves;
-    if (split > 1) {  // few features: the work-group's waves split k
-      if (lds > 0)
-        launch_kernel_lds(rope_rows_kernel<4, true, kD, kW>, grid, block, lds, s, a);
-      else if (rows == 1)
-        launch_kernel(rope_rows_kernel<1, false, kD, kW>, grid, block, s, a);
-      else
-        launch_kernel(rope_rows_kernel<2, false, kD, kW>, grid, block, s, a);
-    } else if (lds > 0) {  // three or four rows of x, staged in LDS
-      launch_kernel_lds(rope_rows_kernel<4, true, kD, 1>, grid, block, lds, s, a);
-    } else if (rows_dot_deep(rows, k)) {  // one or two rows of x, read from L2
-      launch_kernel(rope_rows_kernel<1, false, kRowsDotDeepDepth, 1>, grid, block, s, a);
-    } else if (rows == 1) {
-      launch_kernel(rope_rows_kernel<1, false, kD, 1>, grid, block, s, a);
-    } else {
-      launch_kernel(rope_rows_kernel<2, false, kD, 1>, grid, block, s, a);
-    }
-    return hipGetLastError();
-  }
+  if (fast && rows_dot_applies(rows, k, n0 + n1))
+    return launch_rows(x, w0, w1, nullptr, rows, k, n0, n1, 0, d_r, pos, theta, base, dst, nullptr, s);
   if (fast) {
     hipError_t e = launch_proj_partial(x, w0, w1, rows, k, n0 + n1, n0, part, s);
     if (e != hipSuccess) return e;
@@ -349,6 +370,51 @@ hipError_t launch_query_project(const QueryLaunch& p, const LaunchCtx& s) {
   const int n0 = p.h * p.d_h, n1 = p.h * p.d_r;
   return run_stage(cq, p.w_uq, p.w_qr, p.rows, p.d_qc, n0, n1, p.d_r, p.pos, p.theta, p.base, dst, p.bf16,
                    stage_fast(p.d_qc, n0, n1, p.d_r, p.bf16), static_cast<float*>(part), s);
+}
+
+bool token_project_fused(int rows, int d_model, int d_c, int d_r, int d_qc, int h, int d_h, bool bf16) {
+  return cache_append_fast(d_model, d_c, d_r, bf16) && stage_fast(d_qc, h * d_h, h * d_r, d_r, bf16) &&
+         d_qc % 64 == 0 && rows_dot_applies(rows, d_model, d_c + d_r + d_qc) &&
+         rows_dot_applies(rows, d_qc, h * (d_h + d_r));
+}
+
+size_t token_project_workspace_bytes(int rows, int d_model, int d_c, int d_r, int d_qc, int h, int d_h, bool bf16) {
+  if (token_project_fused(rows, d_model, d_c, d_r, d_qc, h, d_h, bf16)) return align256((size_t)rows * d_qc * 2);
+  const size_t a = cache_append_workspace_bytes(rows, d_model, d_c, d_r, bf16);
+  const size_t q = query_project_workspace_bytes(rows, d_model, d_qc, h, d_h, d_r, bf16);
+  return a > q ? a : q;
+}
+
+hipError_t launch_token_project(const AppendLaunch& ap, const QueryLaunch& qp, const LaunchCtx& s) {
+  if (ap.rows == 0) return hipSuccess;
+  if (!token_project_fused(ap.rows, ap.d_model, ap.d_c, ap.d_r, qp.d_qc, qp.h, qp.d_h, ap.bf16)) {
+    const hipError_t e = launch_cache_append(ap, s);  // the workspace is free again when it ends
+    return e != hipSuccess ? e : launch_query_project(qp, s);
+  }
+  // stage 1: the latent and RoPE key into the pools, c_Q (bf16) into the workspace
+  Dest pool;
+  pool.out0 = ap.latent_pool;
+  pool.out1 = ap.rope_pool;
+  pool.seq = ap.seq;
+  pool.page_table = ap.page_table;
+  pool.max_pages = ap.max_pages;
+  pool.page_size = ap.page_size;
+  pool.num_pages = ap.num_pages;
+  pool.paged = true;
+  void* cq = qp.work;
+  hipError_t e = launch_rows(ap.x, ap.w_dkv, ap.w_kr, qp.w_dq, ap.rows, ap.d_model, ap.d_c, ap.d_r, qp.d_qc, ap.d_r,
+                             ap.pos, ap.theta, ap.base, pool, cq, s);
+  if (e != hipSuccess) return e;
+  // stage 2: [q; q_R] = [W_UQ; W_QR] c_Q, as in launch_query_project
+  Dest dst;
+  dst.out0 = qp.q;
+  dst.out1 = qp.q_r;
+  dst.seq = nullptr;
+  dst.page_table = nullptr;
+  dst.max_pages = dst.page_size = dst.num_pages = 0;
+  dst.paged = false;
+  return launch_rows(cq, qp.w_uq, qp.w_qr, nullptr, qp.rows, qp.d_qc, qp.h * qp.d_h, qp.h * qp.d_r, 0, qp.d_r, qp.pos,
+                     qp.theta, qp.base, dst, nullptr, s);
 }
 
 }  // namespace mla

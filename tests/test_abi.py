@@ -23,7 +23,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj|cache_append|query_project|prefill)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mla_(?:decode|oproj|cache_append|query_project|token_project|prefill)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_names():
@@ -237,6 +237,27 @@ def test_projections_refuse_bad_calls_on_the_host(L):
                                       workspace_bytes=need - 1, stream=0)
     assert e.value.status == binding.MLA_ERR_WORKSPACE
     assert binding.mla_query_project_run(0, 5120, 1536, 128, 128, 64, *([None] * 7), stream=0) == binding.MLA_OK
+    # both in one call: c_Q only when the first stages share a launch (up to
+    # four rows), else what the two calls in turn need
+    assert binding.mla_token_project_workspace_size(1, 5120, 512, 64, 1536, 128, 128) == 3072
+    assert binding.mla_token_project_workspace_size(8, 5120, 512, 64, 1536, 128, 128) == max(
+        binding.mla_cache_append_workspace_size(8, 5120, 512, 64),
+        binding.mla_query_project_workspace_size(8, 5120, 1536, 128, 128, 64))
+    assert binding.mla_token_project_workspace_size(1, 5120, 512, 63, 1536, 128, 128) == 0  # odd d_r
+    shape = (1, 5120, 512, 64, 1536, 128, 128)
+    with pytest.raises(binding.MLAError) as e:  # NULL tensors
+        binding.mla_token_project_run(*shape, *([None] * 9), 4, 64, 8, *([None] * 4), stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    with pytest.raises(binding.MLAError) as e:  # workspace too small
+        binding.mla_token_project_run(*shape, *([4096] * 9), 4, 64, 8, *([4096] * 4), workspace=4096,
+                                      workspace_bytes=3071, stream=0)
+    assert e.value.status == binding.MLA_ERR_WORKSPACE
+    with pytest.raises(binding.MLAError) as e:  # no pools for the pages
+        binding.mla_token_project_run(*shape, *([4096] * 9), 4, 64, 0, *([4096] * 4), workspace=4096,
+                                      workspace_bytes=3072, stream=0)
+    assert e.value.status == binding.MLA_ERR_INVALID_ARG
+    assert binding.mla_token_project_run(0, *shape[1:], *([None] * 9), 4, 64, 8, *([None] * 4),
+                                         stream=0) == binding.MLA_OK
 
 
 def test_prefill_refuses_bad_calls_on_the_host(L):

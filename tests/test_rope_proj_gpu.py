@@ -186,6 +186,56 @@ def test_query_side_deepseek_v2(torch, rows):
     check(q_r.float().cpu().numpy().astype(np.float64), ref_qr, "bf16", "query side q_R rows=%d" % rows)
 
 
+@pytest.mark.parametrize("rows", [1, 3, 5])
+def test_token_projection_in_one_call(torch, rows):
+    """mla_token_project_run: the cache append and the query side of the
+    same rows in one call (up to four rows the first stages share one
+    launch; five rows run the two calls in turn), against the oracle.  q and
+    q_R equal the query side's own call bit for bit (the same sums in the
+    same order); the pools equal the cache append's own call bit for bit
+    when the two calls run in turn."""
+    rng = np.random.default_rng(470 + rows)
+    case = inputs.make_projections(rows, seed=480 + rows)
+    seqs, page_size, max_pages = 2, 64, 8
+    table = rng.permutation(seqs * max_pages).reshape(seqs, max_pages).astype(np.int32)
+    seq = (np.arange(rows) % seqs).astype(np.int32)
+    pos = rng.choice(page_size * max_pages, size=rows, replace=False).astype(np.int32)
+    dev = {k: _dev(torch, case[k], "bf16") for k in ("x", "w_dkv", "w_kr", "w_dq", "w_uq", "w_qr")}
+    seq_d, pos_d, table_d = (torch.from_numpy(a).cuda() for a in (seq, pos, table))
+    bf = torch.bfloat16
+
+    def outputs():
+        return (torch.zeros((table.size, page_size, 512), dtype=bf, device="cuda"),
+                torch.zeros((table.size, page_size, 64), dtype=bf, device="cuda"),
+                torch.full((rows, 128, 128), float("nan"), dtype=bf, device="cuda"),
+                torch.full((rows, 128, 64), float("nan"), dtype=bf, device="cuda"))
+
+    lat, rp, q, q_r = outputs()
+    need = binding.mla_token_project_workspace_size(rows, 5120, 512, 64, 1536, 128, 128)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    binding.mla_token_project_run(rows, 5120, 512, 64, 1536, 128, 128, dev["x"], dev["w_dkv"], dev["w_kr"],
+                                  dev["w_dq"], dev["w_uq"], dev["w_qr"], seq_d, pos_d, table_d, max_pages, page_size,
+                                  table.size, lat, rp, q, q_r, workspace=ws)
+    lat2, rp2, q2, q_r2 = outputs()
+    binding.CacheAppend(5120, 512, 64, "bf16").run(dev["x"], dev["w_dkv"], dev["w_kr"], seq_d, pos_d, table_d, lat2,
+                                                   rp2)
+    binding.QueryProjection(5120, 1536, 128, 128, 64, "bf16").run(dev["x"], dev["w_dq"], dev["w_uq"], dev["w_qr"],
+                                                                  pos_d, q2, q_r2)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(q_r, q_r2)
+    if rows > 4:
+        assert torch.equal(lat, lat2) and torch.equal(rp, rp2)
+    w = {k: inputs.widen(case[k], "bf16") for k in case if k.startswith("w_") or k == "x"}
+    th = oracle.rope_thetas(64, 10000.0)
+    ref_lat, ref_rp = oracle.cache_append(w["x"], w["w_dkv"], w["w_kr"], seq, pos, th, table, page_size,
+                                          np.zeros((table.size, page_size, 512)), np.zeros((table.size, page_size, 64)))
+    check(lat.float().cpu().numpy().astype(np.float64), ref_lat, "bf16", "token projection latent rows=%d" % rows)
+    check(rp.float().cpu().numpy().astype(np.float64), ref_rp, "bf16", "token projection RoPE key rows=%d" % rows)
+    ref_q, ref_qr = oracle.query_project(w["x"], w["w_dq"], w["w_uq"], w["w_qr"], pos, th)
+    check(q.float().cpu().numpy().astype(np.float64), ref_q, "bf16", "token projection q rows=%d" % rows)
+    check(q_r.float().cpu().numpy().astype(np.float64), ref_qr, "bf16", "token projection q_R rows=%d" % rows)
+
+
 def test_query_side_odd_shape_plain_kernels(torch):
     """bf16 storage off the MFMA shapes (plain kernels for both stages)."""
     case = inputs.make_projections(5, d_model=300, d_c=16, d_r=6, d_qc=70, h=3, d_h=10, seed=460)

@@ -236,6 +236,44 @@ def test_token_projection_in_one_call(torch, rows):
     check(q_r.float().cpu().numpy().astype(np.float64), ref_qr, "bf16", "token projection q_R rows=%d" % rows)
 
 
+def test_token_projection_row_outside_the_table(torch):
+    """A row whose position lies past its page table writes nothing to the
+    pools, but its query is still projected (the shared first stage writes
+    c_Q whatever the page)."""
+    case = inputs.make_projections(2, seed=490)
+    page_size, max_pages = 64, 4
+    table = np.arange(2 * max_pages, dtype=np.int32).reshape(2, max_pages)
+    seq = np.array([0, 1], np.int32)
+    pos = np.array([100, page_size * max_pages + 5], np.int32)  # row 1: page index 4 of 4
+    dev = {k: _dev(torch, case[k], "bf16") for k in ("x", "w_dkv", "w_kr", "w_dq", "w_uq", "w_qr")}
+    seq_d, pos_d, table_d = (torch.from_numpy(a).cuda() for a in (seq, pos, table))
+    bf = torch.bfloat16
+    lat = torch.zeros((table.size, page_size, 512), dtype=bf, device="cuda")
+    rp = torch.zeros((table.size, page_size, 64), dtype=bf, device="cuda")
+    q = torch.full((2, 128, 128), float("nan"), dtype=bf, device="cuda")
+    q_r = torch.full((2, 128, 64), float("nan"), dtype=bf, device="cuda")
+    ws = torch.empty(binding.mla_token_project_workspace_size(2, 5120, 512, 64, 1536, 128, 128), dtype=torch.uint8,
+                     device="cuda")
+    binding.mla_token_project_run(2, 5120, 512, 64, 1536, 128, 128, dev["x"], dev["w_dkv"], dev["w_kr"],
+                                  dev["w_dq"], dev["w_uq"], dev["w_qr"], seq_d, pos_d, table_d, max_pages, page_size,
+                                  table.size, lat, rp, q, q_r, workspace=ws)
+    q2 = torch.full_like(q, float("nan"))
+    q_r2 = torch.full_like(q_r, float("nan"))
+    binding.QueryProjection(5120, 1536, 128, 128, 64, "bf16").run(dev["x"], dev["w_dq"], dev["w_uq"], dev["w_qr"],
+                                                                  pos_d, q2, q_r2)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(q_r, q_r2)
+    # only row 0's pool row was written: page table[0][1], row 100 % 64
+    assert int((lat.view(-1, 512).abs().sum(1) != 0).sum()) == 1
+    assert int((rp.view(-1, 64).abs().sum(1) != 0).sum()) == 1
+    w = {k: inputs.widen(case[k], "bf16") for k in ("x", "w_dkv", "w_kr")}
+    ref_lat, ref_rp = oracle.cache_append(w["x"][:1], w["w_dkv"], w["w_kr"], seq[:1], pos[:1],
+                                          oracle.rope_thetas(64, 10000.0), table, page_size,
+                                          np.zeros((table.size, page_size, 512)), np.zeros((table.size, page_size, 64)))
+    check(lat.float().cpu().numpy().astype(np.float64), ref_lat, "bf16", "token projection latent, one row skipped")
+    check(rp.float().cpu().numpy().astype(np.float64), ref_rp, "bf16", "token projection RoPE key, one row skipped")
+
+
 def test_query_side_odd_shape_plain_kernels(torch):
     """bf16 storage off the MFMA shapes (plain kernels for both stages)."""
     case = inputs.make_projections(5, d_model=300, d_c=16, d_r=6, d_qc=70, h=3, d_h=10, seed=460)
